@@ -1,0 +1,93 @@
+"""Plant plausible mistakes in the oracle (on the CPU, via monkeypatch) and check that the
+pins catch each one.  This shows the pins are sensitive to the errors they guard against."""
+import numpy as np
+import pytest
+
+import test_oracle_attention as TA
+import test_oracle_formats as TF
+import test_oracle_quant as TQ
+from oracle import attention as A
+from oracle import formats as F
+from oracle import quant as Qz
+from oracle import rope as R
+
+
+def _caught(pins):
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            return True
+    return False
+
+
+def _ties_down(a, mags):
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 1, len(mags) - 1)
+    lo = hi - 1
+    idx = np.where(mags[hi] - a < a - mags[lo], hi, lo)
+    idx = np.where(a <= mags[0], 0, idx)
+    return np.where(a >= mags[-1], len(mags) - 1, idx)
+
+
+def _r3_floor(Qv, Kv, Vv, c1, c2, quantize_p=True):
+    raw = Qv @ Kv.T
+    t = F.fl32(raw * float(c1)).astype(np.float64)
+    M = np.floor(np.max(t, axis=1, keepdims=True))             # planted: floor, not ceil
+    p = F.fl32(np.exp2(t - M))
+    l = F.fl32(np.sum(p.astype(np.float64), axis=1))
+    pv = F.e4m3_decode(F.e4m3_encode(p * np.float32(448))) if quantize_p else p * 448.0
+    return F.fl32(pv @ Vv * float(c2) / l.astype(np.float64)[:, None]), M[:, 0], l
+
+
+def _r3_sum_of_quantized(Qv, Kv, Vv, c1, c2, quantize_p=True):
+    raw = Qv @ Kv.T
+    t = F.fl32(raw * float(c1)).astype(np.float64)
+    M = np.ceil(np.max(t, axis=1, keepdims=True))
+    p = F.fl32(np.exp2(t - M))
+    pv = F.e4m3_decode(F.e4m3_encode(p * np.float32(448))) if quantize_p else p * 448.0
+    l = F.fl32(np.sum(pv, axis=1) / 448.0)                     # planted: sum of quantized P
+    return F.fl32(pv @ Vv * float(c2) / l.astype(np.float64)[:, None]), M[:, 0], l
+
+
+def _apply_wrong_sign(x_f32, tab):
+    x = np.asarray(x_f32, dtype=np.float32)
+    c, s = tab[:, :, 0], tab[:, :, 1]
+    y = np.empty_like(x)
+    y[..., 0::2] = x[..., 0::2] * c + x[..., 1::2] * s          # planted: clockwise rotation
+    y[..., 1::2] = x[..., 1::2] * c - x[..., 0::2] * s
+    return y
+
+
+MUTATIONS = {
+    "e4m3/e2m1 ties round down": (lambda mp: mp.setattr(F, "_nearest_code", _ties_down),
+                                  [TF.test_e4m3_encode_midpoints_go_to_even_code,
+                                   TF.test_e2m1_rounding_table]),
+    "fp4 exponent off by one": (lambda mp: mp.setattr(
+        Qz, "e8m0_exponent",
+        lambda a: -127 if a == 0 else max(-127, min(127, int(np.floor(np.log2(a))) - 1))),
+        [TQ.test_fp4_worked_block]),
+    "fp8 scale inverted": (lambda mp: mp.setattr(
+        Qz, "fp8_scales", lambda a: (np.float32(448.0 / a) if a else np.float32(1),
+                                     np.float32(a / 448.0) if a else np.float32(1))),
+        [TQ.test_fp8_scale_rule, TQ.test_fp8_amax_maps_to_max_code]),
+    "row offset uses floor": (lambda mp: mp.setattr(A, "r3_rows", _r3_floor),
+                              [TA._pin_softmax_invariants, TA._pin_r3_against_torch_fp8_cast]),
+    "P scale 256 instead of 448": (lambda mp: mp.setattr(A, "P_SCALE", 256.0),
+                                   [TA._pin_r3_against_torch_fp8_cast]),
+    "row sum of quantized P": (lambda mp: mp.setattr(A, "r3_rows", _r3_sum_of_quantized),
+                               [TA._pin_r3_against_torch_fp8_cast]),
+    "softmax scale dropped": (lambda mp: mp.setattr(
+        A, "constants", lambda s_q, s_k, s_v, sm: (np.float32(float(s_q) * float(s_k) * A.LOG2E),
+                                                   np.float32(float(s_v) / 448.0))),
+        [TA._pin_unquantized_equals_sdpa]),
+    "rope rotates clockwise": (lambda mp: mp.setattr(R, "apply", _apply_wrong_sign),
+                               [TQ.test_rope_rotates_counterclockwise_and_text_unchanged]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    plant, pins = MUTATIONS[name]
+    assert not _caught(pins), "pins must pass on the unmodified oracle"
+    plant(monkeypatch)
+    assert _caught(pins), f"no pin caught: {name}"

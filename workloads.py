@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for quantized attention at FLUX.1 Kontext shapes.
+
+This module holds workload structure and random numbers only: tensor shapes,
+the token composition of one Kontext sequence (text | target image | context
+image), the integer 3-axis token positions, and seeded bf16 draws.  It holds
+none of the quantized-attention arithmetic, so that both the CPU oracle and the
+HIP path take their inputs from it without sharing any of the method's code.
+
+Token layout (NVIDIA blog "Optimizing FLUX.1 Kontext for Image Editing with
+Low-Precision Quantization", section "Workflow and Quantization": the input
+image's tokens are concatenated with the output image's tokens, roughly doubling
+the context; lpnh.cn "Flux.1 Kontext deep dive", sections 1 and 3: latents are
+cut into 2x2 patches and concatenated along the sequence, target tokens sit at
+positions (0, h, w) and context tokens at (i, h, w)).
+
+Values: Q, K, V ~ N(0, 1) in float32 from numpy's PCG64 with
+seed = 1000 * config_index + t (t = 0, 1, 2 for Q, K, V), optionally with 1% of
+the H*d hidden channels (31 of 3072 at H=24, d=128; seed + 3 picks them) scaled
+by 20 to mimic activation outliers, then rounded to bf16 (round to nearest
+even, torch's CPU cast).  Arrays are returned as raw bf16 bit patterns
+(numpy uint16), so both sides read identical bytes.
+"""
+from __future__ import annotations
+
+import dataclasses
+import functools
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "CONFIGS", "config", "qkv_bits", "random_bits", "positions",
+           "bits_to_f32"]
+
+OUTLIER_FRACTION = 0.01
+OUTLIER_GAIN = 20.0
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention workload: shapes, token groups and quantization mode."""
+    index: int              # 1-based config number; seeds derive from it
+    name: str
+    B: int
+    H: int
+    d: int
+    n_text: int
+    target_hw: tuple        # (rows, cols) of the target image's patch grid
+    context_hw: tuple       # (rows, cols) of the context image's patch grid
+    mode: str               # "fp8": per-tensor FP8 Q/K/V; "fp4": FP4 block quant then FP8
+    rope: bool              # 3-axis rotary embedding on Q, K before FP4 quant
+    outliers: bool
+
+    @property
+    def N(self) -> int:
+        return (self.n_text + self.target_hw[0] * self.target_hw[1]
+                + self.context_hw[0] * self.context_hw[1])
+
+    @property
+    def flops(self) -> int:
+        """Dense attention work: 2*N*N*d for QK^T plus 2*N*N*d for P.V, per (b, h)."""
+        return 4 * self.B * self.H * self.N * self.N * self.d
+
+
+CONFIGS = [
+    Workload(1, "tiny_sdpa_n256", 1, 2, 128, 64, (8, 12), (8, 12), "fp8", False, False),
+    Workload(2, "kontext_512x512_n2560", 1, 24, 128, 512, (32, 32), (32, 32), "fp8", False, True),
+    Workload(3, "kontext_1024x1024_n8704_fp8", 1, 24, 128, 512, (64, 64), (64, 64), "fp8", False,
+             True),
+    Workload(4, "kontext_1024x1024_n8704_fp4", 1, 24, 128, 512, (64, 64), (64, 64), "fp4", False,
+             True),
+    Workload(5, "multishape_b4_n4608_rope_fp4", 4, 24, 128, 512, (48, 64), (32, 32), "fp4", True,
+             True),
+]
+
+
+def config(index_or_name) -> Workload:
+    for c in CONFIGS:
+        if c.index == index_or_name or c.name == index_or_name:
+            return c
+    raise KeyError(index_or_name)
+
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the float32 values they denote (exact)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _draw(shape, seed: int) -> np.ndarray:
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape, dtype=np.float32)
+
+
+def _outlier_channels(H: int, d: int, seed: int) -> np.ndarray:
+    n = max(1, int(OUTLIER_FRACTION * H * d))
+    return np.random.Generator(np.random.PCG64(seed)).choice(H * d, size=n, replace=False)
+
+
+def random_bits(B: int, H: int, N: int, d: int, seed: int, outliers: bool = False,
+                scale: float = 1.0) -> np.ndarray:
+    """bf16 bits of a [B, H, N, d] tensor ~ scale * N(0, 1), with optional outlier channels."""
+    x = _draw((B, H, N, d), seed)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    if outliers:
+        for c in _outlier_channels(H, d, seed + 3):
+            x[:, c // d, :, c % d] *= np.float32(OUTLIER_GAIN)
+    return _to_bf16_bits(x)
+
+
+@functools.lru_cache(maxsize=3)
+def qkv_bits(index: int):
+    """(q, k, v) bf16 bit arrays [B, H, N, d] for config `index` (1-based)."""
+    c = config(index)
+    return tuple(random_bits(c.B, c.H, c.N, c.d, 1000 * c.index + t, c.outliers)
+                 for t in range(3))
+
+
+def positions(c: Workload) -> np.ndarray:
+    """int32 [N, 3] token positions: text (0, 0, 0); target (0, h, w); context (1, h, w).
+
+    Grids are row-major over (h, w).  A 1024 (wide) x 768 (tall) target image gives a
+    48 x 64 grid of 2x2-patched latent tokens.
+    """
+    pos = np.zeros((c.N, 3), dtype=np.int32)
+    o = c.n_text
+    for image_index, (gh, gw) in ((0, c.target_hw), (1, c.context_hw)):
+        hh, ww = np.meshgrid(np.arange(gh), np.arange(gw), indexing="ij")
+        n = gh * gw
+        pos[o:o + n, 0] = image_index
+        pos[o:o + n, 1] = hh.reshape(-1)
+        pos[o:o + n, 2] = ww.reshape(-1)
+        o += n
+    return pos
