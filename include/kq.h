@@ -1,0 +1,145 @@
+/*
+ * kq.h — quantized scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the SDPA quantization scheme of the NVIDIA blog
+ * "Optimizing FLUX.1 Kontext for Image Editing with Low-Precision Quantization",
+ * section "Workflow and Quantization" (its four bullets and Fig. 4):
+ *   - Q, K and V are quantized per-tensor FP8 or per-block FP4 (first bullet);
+ *   - BMM1 = Q K^T runs on FP8 inputs and accumulates in higher precision (second bullet);
+ *   - softmax runs in FP32 with no quantization (third bullet);
+ *   - BMM2 = P V runs with per-tensor FP8 (fourth bullet);
+ *   - the quantization nodes are FakeQuantize (quantize, then dequantize) operations and the
+ *     scales are static, fixed by post-training calibration (workflow step 4).
+ * Token positions for the rotary embedding follow lpnh.cn "Flux.1 Kontext deep dive",
+ * sections 1 and 3: target-image tokens at (0, h, w), context-image tokens at (i, h, w).
+ *
+ * Formats: FP8 is OCP E4M3 ("E4M3FN": bias 7, max 448, NaN = S.1111.111, no infinities).
+ * FP4 is OCP MX E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in blocks of 32 consecutive
+ * elements along the last dimension, each block with an E8M0 scale byte (2^(byte-127)).
+ * Every encoder rounds to nearest with ties to the even code, saturates to the largest finite
+ * magnitude, and keeps the input's sign bit (negative values that round to zero give -0).
+ *
+ * Conventions for every entry point below:
+ *   - Pointers named *_dev or documented as device pointers are device memory owned by the
+ *     caller; the library allocates nothing, keeps no mutable global state and is reentrant.
+ *   - Device buffers must be 16-byte aligned unless stated otherwise.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no call synchronizes.
+ *     A fault inside a kernel surfaces at the caller's next synchronization.
+ *   - Arguments are validated before any HIP call.  KQ_ERR_INVALID_ARG: a NULL or misaligned
+ *     pointer, a negative or zero size, a non-finite or non-positive scale.
+ *     KQ_ERR_UNSUPPORTED: a valid request outside what the kernels implement (for example
+ *     d != 128 for attention).  KQ_ERR_HIP: the kernel launch failed (hipGetLastError).
+ *     No exception crosses this interface and nothing aborts.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KQ_OK = 0,
+  KQ_ERR_INVALID_ARG = -1,
+  KQ_ERR_UNSUPPORTED = -2,
+  KQ_ERR_HIP = -3
+} kq_status;
+
+/* Layout flags for FP8 outputs. */
+enum {
+  KQ_LAYOUT_ROWS = 0,       /* same as the input: [rows][d], d contiguous                     */
+  KQ_LAYOUT_TRANSPOSED = 1  /* per (batch, head) transposed: [B*H][d][kq_vt_ld(N)], tokens
+                               contiguous, columns N .. kq_vt_ld(N)-1 written as zero          */
+};
+
+/* Rotary-embedding descriptor for kq_quantize_fp4_block.
+ * cos_sin: device float32 [n_tokens][d/2][2] = (cos, sin) of the angle of each adjacent pair
+ * (build it with kq_rope3_table); row r of the input is token r % n_tokens. */
+typedef struct {
+  const float* cos_sin;
+  int64_t n_tokens;
+} kq_rope3;
+
+/* Human-readable name of a status code (static string). */
+const char* kq_status_string(kq_status status);
+
+/* Row stride, in bytes, of the transposed FP8 layout for a sequence of n_tokens tokens:
+ * n_tokens rounded up to a multiple of 128 (the attention kernel's key tile), or -1 if
+ * n_tokens < 1. */
+int64_t kq_vt_ld(int64_t n_tokens);
+
+/* Host-only.  Static per-tensor FP8 scale from a calibrated amax (blog section "Workflow and
+ * Quantization", FP8 per-tensor bullets; workflow step 4): *scale = fl32(amax / 448) and
+ * *inv_scale = fl32(448 / amax), both single IEEE float32 divisions; amax == 0 gives 1 and 1.
+ * INVALID_ARG for NULL outputs or a negative or non-finite amax. */
+kq_status kq_fp8_scales_from_amax(float amax, float* scale, float* inv_scale);
+
+/* Host-only.  Builds the 3-axis rotary table for integer token positions (lpnh.cn "Flux.1
+ * Kontext deep dive", sections 1 and 3).  positions: host int32 [n_tokens][3] (image index,
+ * h, w); table: host float32 [n_tokens][64][2].  The head dimension 128 is cut into axis
+ * slices of widths 16, 56, 56; pair k of axis a (width d_a) turns by pos_a / theta^(2k/d_a),
+ * evaluated in double precision (pow, cos, sin of the C library) and rounded to float32.
+ * INVALID_ARG for NULL pointers, n_tokens < 1 or theta <= 0. */
+kq_status kq_rope3_table(const int32_t* positions, int64_t n_tokens, double theta, float* table);
+
+/* Calibration (blog workflow step 4, read as a max calibrator):
+ * *amax_dev = max(*amax_dev, max_i |x_i|) over n bf16 values.  x_bf16: device bf16 [n];
+ * amax_dev: device float32 scalar, 4-byte aligned, which the caller
+ * initializes (to 0 for a fresh calibration) — successive calls keep a running maximum.
+ * Inputs must be free of NaN.  n == 0 enqueues nothing. */
+kq_status kq_amax_calibrate(const void* x_bf16, int64_t n, float* amax_dev, hipStream_t stream);
+
+/* Per-tensor FP8 quantization, the BMM input quantizer (blog bullets 2 and 4):
+ * y = E4M3(fl32(x * inv_scale)) for a bf16 tensor of rows x d.
+ * layout KQ_LAYOUT_ROWS: y is uint8 [rows][d]; n_tokens is ignored (pass 0 or rows).
+ * layout KQ_LAYOUT_TRANSPOSED: rows = (B*H) * n_tokens and y is uint8 [B*H][d][kq_vt_ld(n_tokens)]
+ * (the layout kq_attn_quant_fwd reads V in); requires d == 128.
+ * Requires d % 16 == 0 and inv_scale finite and > 0. */
+kq_status kq_quantize_fp8_tensor(const void* x_bf16, int64_t rows, int d, int64_t n_tokens,
+                                 float inv_scale, uint8_t* y_e4m3, int layout,
+                                 hipStream_t stream);
+
+/* Per-block FP4 quantization (blog first bullet and Fig. 4), optionally preceded by the
+ * 3-axis rotary embedding (rope != NULL) and optionally followed by per-tensor FP8 of the
+ * dequantized values.  For each row of d elements (d % 32 == 0; d == 128 with a rotary
+ * table) and each block of 32:
+ *   x'   = rope ? rotate(x) : x, in float32, each product and sum rounded separately;
+ *   e    = clamp(floor(log2(max |x'|)) - 2, -127, 127)  (e = -127 for an all-zero block);
+ *   code = E2M1(x' / 2^e);  dq = E2M1value(code) * 2^e  (exact in bf16).
+ * codes:  device uint8 [rows][d/2], two codes per byte, even element in the low nibble.
+ * scales: device uint8 [rows][d/32], E8M0 byte e + 127 (1-byte aligned).
+ * dq_bf16_or_null: device bf16 [rows][d] or NULL.
+ * fp8_or_null: device uint8 [rows][d] = E4M3(fl32(dq * inv_scale8)) or NULL; inv_scale8 is
+ * ignored when fp8_or_null is NULL.
+ * rope: the table must hold n_tokens rows; rows must be a multiple of n_tokens. */
+kq_status kq_quantize_fp4_block(const void* x_bf16, int64_t rows, int d, uint8_t* codes,
+                                uint8_t* scales_e8m0, void* dq_bf16_or_null,
+                                uint8_t* fp8_or_null, float inv_scale8,
+                                const kq_rope3* rope_or_null, hipStream_t stream);
+
+/* Fused quantized attention forward (blog bullets 2-4, Fig. 4), one (batch, head) per
+ * B*H slice, no mask, d = 128:
+ *   BMM1 on E4M3 Q, K with float32 accumulation; t = raw * c1, c1 = s_q s_k sm_scale log2(e);
+ *   float32 softmax with an integer row offset M = ceil(max t) kept online, p = exp2(t - M);
+ *   P quantized to E4M3 with the static per-tensor scale 1/448 (code = E4M3(448 p));
+ *   BMM2 on the E4M3 P and V codes with float32 accumulation;
+ *   O = acc * (s_v / 448) / sum(p), the row sum taken over the unquantized float32 p.
+ * q8, k8: device uint8 [B*H][N][128].  v8: v_layout KQ_LAYOUT_ROWS → [B*H][N][128] is
+ * UNSUPPORTED; v_layout KQ_LAYOUT_TRANSPOSED → [B*H][128][kq_vt_ld(N)] with zero padding, as
+ * kq_quantize_fp8_tensor writes it.  s_q, s_k, s_v: per-tensor scales (kq_fp8_scales_from_amax);
+ * sm_scale: softmax scale (1/sqrt(128) for these models).
+ * o_f32: device float32 [B*H][N][128].  row_stats_or_null: device float32 [B*H][N][2] =
+ * (M, sum(p)) per query row, or NULL. */
+kq_status kq_attn_quant_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                            int v_layout, int B, int H, int N, int d, float s_q, float s_k,
+                            float s_v, float sm_scale, float* o_f32, float* row_stats_or_null,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

@@ -1,0 +1,208 @@
+"""Python binding of libkq, the quantized-SDPA library for MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI declared in include/kq.h: every function below has
+the name of the C entry point it calls, checks that tensors are contiguous device tensors
+of the expected dtype and size, and passes raw pointers plus the current HIP stream.  All
+arithmetic runs in the library's HIP kernels (or, for the two host-only helpers, in its
+C code).  PyTorch supplies device memory and streams only.
+
+The library must be built (``python -m precision_quantized_attention_amd.build`` or
+``__graft_entry__.build()``); importing works without it, but every call raises
+``KQError`` if ``libkq.so`` is missing.  There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSED",
+           "kq_status_string", "kq_vt_ld", "kq_fp8_scales_from_amax", "kq_rope3_table",
+           "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
+           "kq_attn_quant_fwd"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
+KQ_LAYOUT_ROWS = 0
+KQ_LAYOUT_TRANSPOSED = 1
+
+
+class KQError(RuntimeError):
+    pass
+
+
+class _Rope3(ctypes.Structure):
+    _fields_ = [("cos_sin", ctypes.c_void_p), ("n_tokens", ctypes.c_int64)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "kq_status_string": ([_I], ctypes.c_char_p),
+    "kq_vt_ld": ([_I64], _I64),
+    "kq_fp8_scales_from_amax": ([_F, ctypes.POINTER(_F), ctypes.POINTER(_F)], _I),
+    "kq_rope3_table": ([_P, _I64, ctypes.c_double, _P], _I),
+    "kq_amax_calibrate": ([_P, _I64, _P, _P], _I),
+    "kq_quantize_fp8_tensor": ([_P, _I64, _I, _I64, _F, _P, _I, _P], _I),
+    "kq_quantize_fp4_block": ([_P, _I64, _I, _P, _P, _P, _P, _F, ctypes.POINTER(_Rope3), _P],
+                              _I),
+    "kq_attn_quant_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P], _I),
+}
+
+
+def load():
+    """Load libkq.so (once) and declare its signatures; raises KQError if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KQError(f"{LIB_PATH} is not built; run precision_quantized_attention_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().kq_status_string(status).decode()
+        raise KQError(f"{what}: {msg} ({status})")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise KQError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise KQError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise KQError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, dtype, name):
+    return None if t is None else _dev(t, dtype, name)
+
+
+# ------------------------------------------------------------------ host helpers
+
+def kq_status_string(status: int) -> str:
+    return load().kq_status_string(status).decode()
+
+
+def kq_vt_ld(n_tokens: int) -> int:
+    return int(load().kq_vt_ld(n_tokens))
+
+
+def kq_fp8_scales_from_amax(amax: float):
+    """(scale, inv_scale) as numpy float32 from a calibrated amax (host-only C helper)."""
+    s = _F()
+    inv = _F()
+    _check(load().kq_fp8_scales_from_amax(float(amax), ctypes.byref(s), ctypes.byref(inv)),
+           "kq_fp8_scales_from_amax")
+    return np.float32(s.value), np.float32(inv.value)
+
+
+def kq_rope3_table(positions, theta: float = 10000.0) -> np.ndarray:
+    """float32 [N, 64, 2] (cos, sin) table for int32 positions [N, 3] (host-only C helper)."""
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    if pos.ndim != 2 or pos.shape[1] != 3:
+        raise KQError("positions must be [N, 3]")
+    out = np.empty((pos.shape[0], 64, 2), np.float32)
+    _check(load().kq_rope3_table(pos.ctypes.data_as(_P), pos.shape[0], float(theta),
+                                 out.ctypes.data_as(_P)), "kq_rope3_table")
+    return out
+
+
+# ------------------------------------------------------------------ device entry points
+
+def kq_amax_calibrate(x, amax, stream=None):
+    """amax[0] = max(amax[0], max|x|); x bf16 device tensor, amax float32 device tensor [1]."""
+    import torch
+    if amax.numel() != 1:
+        raise KQError("amax must hold one float32")
+    _check(load().kq_amax_calibrate(_dev(x, torch.bfloat16, "x"), x.numel(),
+                                    _dev(amax, torch.float32, "amax"), _stream(stream)),
+           "kq_amax_calibrate")
+
+
+def kq_quantize_fp8_tensor(x, inv_scale: float, y, layout: int = KQ_LAYOUT_ROWS,
+                           n_tokens: int = 0, stream=None):
+    """E4M3 codes of x * inv_scale into y (uint8).  x: bf16 [..., d].
+    layout KQ_LAYOUT_ROWS: y has x's shape.  KQ_LAYOUT_TRANSPOSED: x is [B, H, N, d] (or any
+    [rows, d] with rows = BH * n_tokens) and y is [BH, d, kq_vt_ld(N)]."""
+    import torch
+    d = x.shape[-1]
+    rows = x.numel() // d
+    if layout == KQ_LAYOUT_ROWS:
+        if y.numel() != x.numel():
+            raise KQError("y must have as many elements as x")
+    else:
+        if n_tokens <= 0:
+            n_tokens = x.shape[-2]
+        if rows % n_tokens:
+            raise KQError("rows must be a multiple of n_tokens")
+        if y.numel() != (rows // n_tokens) * d * kq_vt_ld(n_tokens):
+            raise KQError("y must be [B*H, d, kq_vt_ld(N)]")
+    _check(load().kq_quantize_fp8_tensor(_dev(x, torch.bfloat16, "x"), rows, d, n_tokens,
+                                         float(inv_scale), _dev(y, torch.uint8, "y"), layout,
+                                         _stream(stream)), "kq_quantize_fp8_tensor")
+
+
+def kq_quantize_fp4_block(x, codes, scales, dq=None, fp8=None, inv_scale8: float = 1.0,
+                          rope=None, stream=None):
+    """FP4 E2M1 block quantization of x (bf16 [..., d]).
+    codes uint8 [..., d/2]; scales uint8 [..., d/32]; dq bf16 like x or None; fp8 uint8 like x
+    or None; rope = (table float32 device tensor [N, 64, 2], N) or None."""
+    import torch
+    d = x.shape[-1]
+    rows = x.numel() // d
+    if codes.numel() != rows * d // 2 or scales.numel() != rows * d // 32:
+        raise KQError("codes must be [rows, d/2] and scales [rows, d/32]")
+    for t, nm in ((dq, "dq"), (fp8, "fp8")):
+        if t is not None and t.numel() != x.numel():
+            raise KQError(f"{nm} must have as many elements as x")
+    rp = None
+    if rope is not None:
+        table, n_tok = rope
+        if table.numel() != n_tok * d:
+            raise KQError("rope table must be [N, d/2, 2]")
+        rp = ctypes.byref(_Rope3(_dev(table, torch.float32, "rope table"), int(n_tok)))
+    _check(load().kq_quantize_fp4_block(
+        _dev(x, torch.bfloat16, "x"), rows, d, _dev(codes, torch.uint8, "codes"),
+        _dev(scales, torch.uint8, "scales"), _opt(dq, torch.bfloat16, "dq"),
+        _opt(fp8, torch.uint8, "fp8"), float(inv_scale8), rp, _stream(stream)),
+        "kq_quantize_fp4_block")
+
+
+def kq_attn_quant_fwd(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float, o,
+                      row_stats=None, v_layout: int = KQ_LAYOUT_TRANSPOSED, stream=None):
+    """Fused quantized attention.  q8, k8: uint8 [B, H, N, d]; v8t: uint8 [B*H, d, kq_vt_ld(N)];
+    o: float32 [B, H, N, d]; row_stats: float32 [B, H, N, 2] or None."""
+    import torch
+    B, H, N, d = q8.shape
+    if tuple(k8.shape) != (B, H, N, d) or tuple(o.shape) != (B, H, N, d):
+        raise KQError("k8 and o must match q8's shape")
+    if v_layout == KQ_LAYOUT_TRANSPOSED and v8t.numel() != B * H * d * kq_vt_ld(N):
+        raise KQError("v8t must be [B*H, d, kq_vt_ld(N)]")
+    if row_stats is not None and row_stats.numel() != B * H * N * 2:
+        raise KQError("row_stats must be [B, H, N, 2]")
+    _check(load().kq_attn_quant_fwd(
+        _dev(q8, torch.uint8, "q8"), _dev(k8, torch.uint8, "k8"), _dev(v8t, torch.uint8, "v8"),
+        v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
+        _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"),
+        _stream(stream)), "kq_attn_quant_fwd")

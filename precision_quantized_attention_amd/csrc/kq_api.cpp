@@ -1,0 +1,158 @@
+// C-ABI entry points of libkq: argument validation (before any HIP call), the host-side scale
+// and rotary-table rules, and dispatch to the HIP kernels.  See include/kq.h for the contract.
+
+#include "../../include/kq.h"
+#include "kq_launch.h"
+
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool finite_pos(float x) { return isfinite(x) && x > 0.0f; }
+kq_status from_hip(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_HIP; }
+
+constexpr int64_t kVtAlign = 128;
+constexpr int kAxes[3] = {16, 56, 56};
+
+}  // namespace
+
+extern "C" {
+
+const char* kq_status_string(kq_status status) {
+  switch (status) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_INVALID_ARG: return "invalid argument";
+    case KQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KQ_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int64_t kq_vt_ld(int64_t n_tokens) {
+  if (n_tokens < 1) return -1;
+  return (n_tokens + kVtAlign - 1) / kVtAlign * kVtAlign;
+}
+
+kq_status kq_fp8_scales_from_amax(float amax, float* scale, float* inv_scale) {
+  if (scale == nullptr || inv_scale == nullptr) return KQ_ERR_INVALID_ARG;
+  if (!isfinite(amax) || amax < 0.0f) return KQ_ERR_INVALID_ARG;
+  if (amax == 0.0f) {
+    *scale = 1.0f;
+    *inv_scale = 1.0f;
+    return KQ_OK;
+  }
+  volatile float a = amax;              // keep each division a single float32 operation
+  *scale = a / 448.0f;
+  *inv_scale = 448.0f / a;
+  return KQ_OK;
+}
+
+kq_status kq_rope3_table(const int32_t* positions, int64_t n_tokens, double theta, float* table) {
+  if (positions == nullptr || table == nullptr || n_tokens < 1) return KQ_ERR_INVALID_ARG;
+  if (!(theta > 0.0) || !isfinite(theta)) return KQ_ERR_INVALID_ARG;
+  for (int64_t n = 0; n < n_tokens; ++n) {
+    int j = 0;
+    for (int a = 0; a < 3; ++a) {
+      const double p = (double)positions[n * 3 + a];
+      const int da = kAxes[a];
+      for (int k = 0; k < da / 2; ++k) {
+        const double w = 1.0 / pow(theta, (2.0 * k) / da);
+        const double ang = p * w;
+        table[(n * 64 + j) * 2 + 0] = (float)cos(ang);
+        table[(n * 64 + j) * 2 + 1] = (float)sin(ang);
+        ++j;
+      }
+    }
+  }
+  return KQ_OK;
+}
+
+kq_status kq_amax_calibrate(const void* x_bf16, int64_t n, float* amax_dev, hipStream_t stream) {
+  if (x_bf16 == nullptr || amax_dev == nullptr || n < 0) return KQ_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(amax_dev, 4)) return KQ_ERR_INVALID_ARG;
+  if (n == 0) return KQ_OK;
+  return from_hip(kq::launch_amax_bf16(static_cast<const uint16_t*>(x_bf16), n, amax_dev, stream));
+}
+
+kq_status kq_quantize_fp8_tensor(const void* x_bf16, int64_t rows, int d, int64_t n_tokens,
+                                 float inv_scale, uint8_t* y_e4m3, int layout,
+                                 hipStream_t stream) {
+  if (x_bf16 == nullptr || y_e4m3 == nullptr || rows < 1 || d < 1) return KQ_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(y_e4m3, 16) || !finite_pos(inv_scale))
+    return KQ_ERR_INVALID_ARG;
+  if (d % 16 != 0) return KQ_ERR_UNSUPPORTED;
+  if (layout == KQ_LAYOUT_ROWS) {
+    return from_hip(kq::launch_fp8_rows(static_cast<const uint16_t*>(x_bf16), rows * d,
+                                        inv_scale, y_e4m3, stream));
+  }
+  if (layout != KQ_LAYOUT_TRANSPOSED) return KQ_ERR_INVALID_ARG;
+  if (n_tokens < 1 || rows % n_tokens != 0) return KQ_ERR_INVALID_ARG;
+  if (d != 128) return KQ_ERR_UNSUPPORTED;
+  const int64_t bh = rows / n_tokens;
+  if (bh > 65535) return KQ_ERR_UNSUPPORTED;
+  return from_hip(kq::launch_fp8_transposed(static_cast<const uint16_t*>(x_bf16), bh, n_tokens,
+                                            kq_vt_ld(n_tokens), inv_scale, y_e4m3, stream));
+}
+
+kq_status kq_quantize_fp4_block(const void* x_bf16, int64_t rows, int d, uint8_t* codes,
+                                uint8_t* scales_e8m0, void* dq_bf16_or_null,
+                                uint8_t* fp8_or_null, float inv_scale8,
+                                const kq_rope3* rope_or_null, hipStream_t stream) {
+  if (x_bf16 == nullptr || codes == nullptr || scales_e8m0 == nullptr || rows < 1 || d < 1)
+    return KQ_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(codes, 16)) return KQ_ERR_INVALID_ARG;
+  if (dq_bf16_or_null != nullptr && !aligned(dq_bf16_or_null, 16)) return KQ_ERR_INVALID_ARG;
+  if (fp8_or_null != nullptr && (!aligned(fp8_or_null, 16) || !finite_pos(inv_scale8)))
+    return KQ_ERR_INVALID_ARG;
+  if (d % 32 != 0) return KQ_ERR_UNSUPPORTED;
+  const float* table = nullptr;
+  int64_t tokens = 1;
+  if (rope_or_null != nullptr) {
+    if (rope_or_null->cos_sin == nullptr || rope_or_null->n_tokens < 1) return KQ_ERR_INVALID_ARG;
+    if (!aligned(rope_or_null->cos_sin, 16)) return KQ_ERR_INVALID_ARG;
+    if (rows % rope_or_null->n_tokens != 0) return KQ_ERR_INVALID_ARG;
+    if (d != 128) return KQ_ERR_UNSUPPORTED;
+    table = rope_or_null->cos_sin;
+    tokens = rope_or_null->n_tokens;
+  }
+  if (rows * (int64_t)d / 8 > (int64_t)UINT32_MAX * 256) return KQ_ERR_UNSUPPORTED;
+  return from_hip(kq::launch_fp4_block(static_cast<const uint16_t*>(x_bf16), rows, d, codes,
+                                       scales_e8m0, static_cast<uint16_t*>(dq_bf16_or_null),
+                                       fp8_or_null, inv_scale8, table, tokens, stream));
+}
+
+kq_status kq_attn_quant_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                            int v_layout, int B, int H, int N, int d, float s_q, float s_k,
+                            float s_v, float sm_scale, float* o_f32, float* row_stats_or_null,
+                            hipStream_t stream) {
+  if (q8 == nullptr || k8 == nullptr || v8 == nullptr || o_f32 == nullptr) return KQ_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return KQ_ERR_INVALID_ARG;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o_f32, 16))
+    return KQ_ERR_INVALID_ARG;
+  if (row_stats_or_null != nullptr && !aligned(row_stats_or_null, 8)) return KQ_ERR_INVALID_ARG;
+  if (!finite_pos(s_q) || !finite_pos(s_k) || !finite_pos(s_v) || !finite_pos(sm_scale))
+    return KQ_ERR_INVALID_ARG;
+  if (v_layout != KQ_LAYOUT_ROWS && v_layout != KQ_LAYOUT_TRANSPOSED) return KQ_ERR_INVALID_ARG;
+  if (d != 128 || v_layout != KQ_LAYOUT_TRANSPOSED) return KQ_ERR_UNSUPPORTED;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t nqb = ((int64_t)N + 127) / 128;
+  if (bh * nqb > INT32_MAX || bh * (int64_t)N * 128 > ((int64_t)1 << 40)) return KQ_ERR_UNSUPPORTED;
+  const double c1 = (double)s_q * (double)s_k * (double)sm_scale * 1.4426950408889634;
+  if (!isfinite(c1) || !isfinite((float)c1) || (float)c1 <= 0.0f) return KQ_ERR_INVALID_ARG;
+  kq::AttnParams p;
+  p.q = q8;
+  p.k = k8;
+  p.vt = v8;
+  p.o = o_f32;
+  p.stats = row_stats_or_null;
+  p.bh = (int)bh;
+  p.n = N;
+  p.ldv = kq_vt_ld(N);
+  p.c1 = (float)c1;
+  p.s_v = s_v;
+  return from_hip(kq::launch_attn_fp8(p, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Internal launchers shared by the C-ABI layer (kq_api.cpp) and the kernel files.
+// Arguments arrive here already validated; each launcher enqueues its kernels on `stream`
+// and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream);
+
+hipError_t launch_fp8_rows(const uint16_t* x, int64_t n, float inv_scale, uint8_t* y,
+                           hipStream_t stream);
+
+hipError_t launch_fp8_transposed(const uint16_t* x, int64_t bh, int64_t n_tokens, int64_t ld,
+                                 float inv_scale, uint8_t* y, hipStream_t stream);
+
+hipError_t launch_fp4_block(const uint16_t* x, int64_t rows, int d, uint8_t* codes,
+                            uint8_t* scales, uint16_t* dq, uint8_t* fp8, float inv_scale8,
+                            const float* rope_table, int64_t rope_tokens, hipStream_t stream);
+
+struct AttnParams {
+  const uint8_t* q;       // [BH][N][128] E4M3
+  const uint8_t* k;       // [BH][N][128] E4M3
+  const uint8_t* vt;      // [BH][128][ldv] E4M3, zero beyond N
+  float* o;               // [BH][N][128]
+  float* stats;           // [BH][N][2] or nullptr
+  int bh;
+  int n;
+  int64_t ldv;
+  float c1;               // s_q * s_k * sm_scale * log2(e), rounded once to float32
+  float s_v;
+};
+
+hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream);
+
+}  // namespace kq

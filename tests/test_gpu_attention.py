@@ -1,0 +1,156 @@
+"""GPU parity of the fused quantized attention against the oracle (R3).
+
+Whole path per workload: calibration (static scales) -> quantization -> attention, with the
+FP8 inputs compared bit-exactly and the output within rel-L2 1e-2 and max-abs 5e-2 of the
+oracle.  At full size the oracle evaluates sampled query rows (each row is independent).
+The error against unquantized float64 attention is printed, not gated.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import precision_quantized_attention_amd as kq
+import workloads as W
+from kq_testutil import MAX_ABS_TOL, REL_L2_TOL, max_abs, rel_l2, sample_rows, to_dev
+from oracle import attention as A
+from oracle import pipeline as OP
+from precision_quantized_attention_amd.pipeline import QuantizedSDPA
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(bits, mode="fp8", positions=None, stats=False):
+    B, H, N, d = bits[0].shape
+    x = [to_dev(b) for b in bits]
+    m = QuantizedSDPA(B, H, N, d, mode=mode, positions=positions, want_stats=stats)
+    m.calibrate(*x)
+    o = m.forward(*x)
+    torch.cuda.synchronize()
+    return m, o
+
+
+def _check_codes(m, qz):
+    c = m.buf
+    assert np.array_equal(c.q8.cpu().numpy(), qz.codes["q"])
+    assert np.array_equal(c.k8.cpu().numpy(), qz.codes["k"])
+    B, H, N, d = qz.codes["v"].shape
+    vt = c.v8t.cpu().numpy()[:, :, :N].transpose(0, 2, 1).reshape(B, H, N, d)
+    assert np.array_equal(vt, qz.codes["v"])
+    assert not np.any(c.v8t.cpu().numpy()[:, :, N:])
+
+
+def _compare(o_gpu, o_ref, label):
+    e, a = rel_l2(o_gpu, o_ref), max_abs(o_gpu, o_ref)
+    print(f"{label}: rel_l2 {e:.3e} max_abs {a:.3e} (|O| max {np.abs(o_ref).max():.3g})",
+          flush=True)
+    assert e <= REL_L2_TOL, (label, e)
+    assert a <= MAX_ABS_TOL, (label, a)
+    return e, a
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_attention_config(cfg):
+    c = W.config(cfg)
+    print(f"attention cfg{cfg} {c.name} B={c.B} H={c.H} N={c.N} mode={c.mode} rope={c.rope}",
+          flush=True)
+    bits = W.qkv_bits(cfg)
+    pos = W.positions(c) if c.rope else None
+    m, o = _run(bits, mode=c.mode, positions=pos, stats=True)
+    qz = OP.quantize_inputs(*bits, mode=c.mode, positions=pos)
+    for n in "qkv":
+        assert m.amax[n] == qz.amax[n] and m.scales[n] == qz.scale[n]
+    _check_codes(m, qz)
+    if cfg == 1:
+        rows, heads = np.arange(c.N), [(b, h) for b in range(c.B) for h in range(c.H)]
+    else:
+        rows = sample_rows(c.N, 24, seed=cfg)
+        heads = [(0, 0), (c.B - 1, c.H - 1), (c.B // 2, 7 % c.H)]
+    o_np = o.cpu().numpy()
+    stats = m.buf.stats.cpu().numpy()
+    sub = {n: np.stack([qz.codes[n][b, h] for b, h in heads])[None] for n in "qkv"}
+    O, M, L = A.attention_r3(sub["q"], sub["k"], sub["v"], qz.scale["q"][0], qz.scale["k"][0],
+                             qz.scale["v"][0], m.sm_scale, rows=rows)
+    got = np.stack([o_np[b, h][rows] for b, h in heads])
+    _compare(got, O[0], f"cfg{cfg} vs oracle")
+    # row statistics: same offset up to a float32 tie at an integer, same 2^M * l
+    st = np.stack([stats[b, h][rows] for b, h in heads])
+    assert np.all(np.abs(st[..., 0] - M[0]) <= 1)
+    tot_gpu = st[..., 1].astype(np.float64) * np.exp2(st[..., 0])
+    tot_ref = L[0].astype(np.float64) * np.exp2(M[0])
+    assert np.allclose(tot_gpu, tot_ref, rtol=1e-2)
+    # reported, not gated: error of the quantized path against float64 attention
+    xs = [W.bits_to_f32(b) for b in bits]
+    if c.rope:
+        from oracle import rope as R
+        tab = R.table(pos)
+        xs[0], xs[1] = R.apply(xs[0], tab), R.apply(xs[1], tab)
+    sel = [np.stack([x[b, h] for b, h in heads])[None] for x in xs]
+    ref64 = A.attention_fp64(sel[0], sel[1], sel[2], 1 / math.sqrt(128), rows=rows)
+    print(f"cfg{cfg} vs unquantized fp64: rel_l2 {rel_l2(got, ref64[0]):.3e} "
+          f"(oracle itself: {rel_l2(O[0], ref64[0]):.3e})", flush=True)
+
+
+@pytest.mark.parametrize("N", [1, 2, 5, 63, 64, 65, 127, 128, 129, 255, 257, 1000])
+def test_attention_ragged_lengths(N):
+    print(f"ragged N={N}", flush=True)
+    bits = [W.random_bits(1, 2, N, 128, seed=500 + 3 * N + t, outliers=(N > 100)) for t in range(3)]
+    m, o = _run(bits)
+    qz = OP.quantize_inputs(*bits)
+    _check_codes(m, qz)
+    O, _, _ = OP.attention(qz)
+    _compare(o.cpu().numpy(), O, f"N={N}")
+
+
+def test_attention_batch_heads_and_fp4_small():
+    print("B=2 H=3 N=300 fp4+rope", flush=True)
+    c = W.config(5)
+    pos = W.positions(c)[450:750]
+    bits = [W.random_bits(2, 3, 300, 128, seed=800 + t, outliers=True) for t in range(3)]
+    m, o = _run(bits, mode="fp4", positions=pos)
+    qz = OP.quantize_inputs(*bits, mode="fp4", positions=pos)
+    _check_codes(m, qz)
+    O, _, _ = OP.attention(qz)
+    _compare(o.cpu().numpy(), O, "B2H3 fp4 rope")
+
+
+def test_attention_deterministic():
+    bits = [b[:, :4] for b in W.qkv_bits(2)]
+    m, o1 = _run(bits)
+    o1 = o1.clone()
+    o2 = m.forward(*[to_dev(b) for b in bits])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_attention_rejects_row_layout_v():
+    x = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device="cuda")
+    o = torch.empty((1, 1, 64, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(kq.KQError):
+        kq.kq_attn_quant_fwd(x, x, x, 1.0, 1.0, 1.0, 0.1, o, v_layout=kq.KQ_LAYOUT_ROWS)
+
+
+def test_attention_every_e4m3_code_in_q_and_k():
+    """Q and K holding every finite E4M3 code (both signs, subnormals, +-448): the kernel's
+    on-chip conversion of the codes for the first product must be exact."""
+    import oracle.formats as F
+    N, d = 256, 128
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    rng = np.random.default_rng(5)
+    q8 = rng.choice(codes, size=(1, 1, N, d)).astype(np.uint8)
+    k8 = rng.choice(codes, size=(1, 1, N, d)).astype(np.uint8)
+    v8 = rng.choice(codes, size=(1, 1, N, d)).astype(np.uint8)
+    s_q = s_k = np.float32(2.0 ** -9)             # keep t = raw * c1 in a moderate range
+    s_v = np.float32(1.0 / 64)
+    sm = np.float32(1 / math.sqrt(128))
+    ld = kq.kq_vt_ld(N)
+    vt = np.zeros((1, d, ld), np.uint8)
+    vt[0, :, :N] = v8[0, 0].T
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q8, k8, vt))
+    o = torch.empty((1, 1, N, d), dtype=torch.float32, device="cuda")
+    kq.kq_attn_quant_fwd(dq, dk, dv, s_q, s_k, s_v, sm, o)
+    torch.cuda.synchronize()
+    O, _, _ = A.attention_r3(q8, k8, v8, s_q, s_k, s_v, sm)
+    _compare(o.cpu().numpy(), O, "every E4M3 code")
+    assert F.e4m3_decode(codes).max() == 448.0
