@@ -20,17 +20,20 @@
 // FP8 MFMA (v_mfma_f32_32x32x64_f8f6f4): there the truncation only touches products of tiny
 // probabilities, far below the output tolerance.
 //
-// Work decomposition (CDNA4, wave64): workgroup = 4 waves = 128 query rows of one
-// (batch, head); wave = 32 query rows; key tiles of 64 keys.  Per tile the workgroup stages
-// K (converted to bf16, [64][128]) and V^T (FP8, [128][64]) in LDS, double buffered, one
-// barrier per tile.  Both products are computed transposed so each lane owns one query row:
+// Work decomposition (CDNA4, wave64): workgroup = 8 waves = 256 query rows of one
+// (batch, head), one workgroup per CU; wave = 32 query rows; key tiles of 64 keys.  Per tile
+// the workgroup stages K (converted to bf16, [64][128]) and V^T (FP8, [128][64]) in LDS,
+// double buffered.  The two waves sharing a SIMD run in ping-pong: while one issues matrix-core
+// work the other runs its softmax on the VALU (see the schedule in the kernel).  Both products are computed transposed so each lane owns one query row:
 //   S^T (keys x queries) = K · Q^T      A = K rows from LDS, B = Q (registers, loaded once)
 //   O^T (d x queries)   += V^T · P^T    A = V^T rows from LDS, B = P (registers)
 // so the S accumulator of lane (r, g) holds 32 scores of query r, which is exactly the B
 // operand layout P needs for the second product: no cross-lane shuffles of P, and the row
 // max / row sum need one exchange between lanes r and r + 32.  The K rows fed to the first
-// product are permuted (krow below) so that lane group g ends up holding the 32 consecutive
+// product are permuted (krow_of_key) so that lane group g ends up holding the 32 consecutive
 // keys 32g .. 32g + 31 of the tile; V^T then supplies them as one contiguous 32-byte run.
+// LDS rows are padded by 16 bytes, which spreads the operand reads of any 8 (or 16)
+// consecutive lanes over distinct 16-byte bank slots.
 
 #include "kq_launch.h"
 
@@ -47,19 +50,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
-constexpr int kBM = 128;        // query rows per workgroup
-constexpr int kBN = 64;         // keys per tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                   // two groups of four waves, one wave per SIMD each
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKRow = kD * 2;   // bytes per bf16 K row in LDS
+constexpr int kBM = 32 * kWaves;            // query rows per workgroup (32 per wave)
+constexpr int kBN = 64;                     // keys per tile
+constexpr int kKPitch = kD * 2 + 16;        // bf16 K row in LDS + 16 bytes of padding
+constexpr int kVPitch = kBN + 16;           // FP8 V^T row in LDS + 16 bytes of padding
+constexpr int kKStage = kBN * kKPitch;      // 17408 bytes
+constexpr int kVStage = kD * kVPitch;       // 10240 bytes
 constexpr float kLog2_448 = 8.807354922057604f;
-
-// LDS swizzles of 16-byte chunks (XOR on the chunk index) so that the operand reads of any
-// 8 consecutive lanes hit 8 different 16-byte slots of a 128-byte bank window.
-__device__ __forceinline__ int kswz(int row) {
-  return (row & 3) | (((row >> 5) & 1) << 2) | (((row >> 2) & 1) << 3);
-}
-__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 3; }
 
 // Buffer resource over `bytes` bytes from `base`: loads past the end return zeros (the
 // hardware range check), which pads the last key tile and the last query block.
@@ -86,9 +85,11 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
 __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
-  // format codes 0, 0: both operands OCP E4M3; no block scaling
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// FP8 x FP8 with E8M0 block scales on the B operand (format codes 0, 0: both operands OCP
+// E4M3; A unscaled, 127 = 1.0).  The 64 k-values form two scale blocks: bytes 0-15 of both
+// lane groups are block 0 and bytes 16-31 block 1; lane group g supplies block g's scale.
+__device__ __forceinline__ v16f mfma_f8_scaled(v8i a, v8i b, v16f c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
 
 __device__ __forceinline__ v8i cat8(uint4 lo, uint4 hi) {
@@ -99,9 +100,23 @@ __device__ __forceinline__ v8i cat8(uint4 lo, uint4 hi) {
 }
 __device__ __forceinline__ v8bf as_bf16x8(uint4 v) { return __builtin_bit_cast(v8bf, v); }
 
-__global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnParams a, int nqb) {
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kBN * kKRow];   // bf16 K tiles
-  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][kD * kBN];      // FP8 V^T tiles
+// max(x[l], x[l ^ 32]) for every lane l: v_permlane32_swap with both operands x leaves
+// {x[l], x[l ^ 32]} in its two results (in an order that depends on the half of the wave).
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// LDS row of key kappa (0..63 within a tile): rows are stored in the order the first product
+// consumes them — row 32kb + r feeds lane r of key block kb (see the file comment for the
+// key permutation), so every operand read is a fixed per-lane base plus an immediate offset.
+__device__ __forceinline__ int krow_of_key(int kappa) {
+  return 32 * ((kappa >> 4) & 1) + 8 * ((kappa >> 2) & 3) + 4 * ((kappa >> 5) & 1) + (kappa & 3);
+}
+
+__global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int nqb) {
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * kKStage];   // bf16 K tiles
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[2 * kVStage];   // FP8 V^T tiles
 
   // XCD-aware order: consecutive dispatch slots go round-robin over the 8 XCDs, so give each
   // XCD a contiguous range of (head, query-block) pairs and keep a head's K/V in one L2.
@@ -109,9 +124,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnParams a, int
   const int xcd = bid & 7, local = bid >> 3, per = total >> 3, rem = total & 7;
   const int logical = (xcd < rem) ? xcd * (per + 1) + local
                                   : rem * (per + 1) + (xcd - rem) * per + local;
-  const int bh = logical / nqb, qb = logical - bh * nqb;
+  // (the integer division runs on the vector unit; readfirstlane returns the values to scalar
+  // registers so the buffer descriptors below stay scalar)
+  const int bh = __builtin_amdgcn_readfirstlane(logical / nqb);
+  const int qb = logical - bh * nqb;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, g = l >> 5;
+  const int grp = w >> 2;                   // 0: waves 0-3, 1: waves 4-7 (one per SIMD each)
   const int N = a.n;
   const int q = qb * kBM + w * 32 + r;
 
@@ -129,153 +148,188 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnParams a, int
     }
   }
 
-  // K row (within the tile) read by this lane for key block kb (see file comment).
-  int kbase[2], ksw[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int krow = 32 * ((r >> 2) & 1) + 16 * kb + 4 * (r >> 3) + (r & 3);
-    kbase[kb] = krow * kKRow;
-    ksw[kb] = kswz(krow);
-  }
+  // Operand read bases (bytes within a stage); block kb / step m / d-block c are immediates.
+  const int kread = r * kKPitch + 16 * g;
+  const int vread = r * kVPitch + 32 * g;
 
-  // Tile loader: each thread moves two 16-byte FP8 chunks of K (written as 2 x 16 bytes of
-  // bf16 to LDS) and two 16-byte chunks of V^T per tile.
-  const int kr0 = tid >> 3, kc = tid & 7;                  // K chunk tid: row, 16-byte column
-  const int kr1 = kr0 + kThreads / 8;                      // K chunk tid + 256
-  const int vd0 = tid >> 2, vc = tid & 3;                  // V^T chunk tid
-  const int vd1 = vd0 + kThreads / 4;
-  const int ks00 = kr0 * kKRow + (((2 * kc) ^ kswz(kr0)) << 4);
-  const int ks01 = kr0 * kKRow + (((2 * kc + 1) ^ kswz(kr0)) << 4);
-  const int ks10 = kr1 * kKRow + (((2 * kc) ^ kswz(kr1)) << 4);
-  const int ks11 = kr1 * kKRow + (((2 * kc + 1) ^ kswz(kr1)) << 4);
-  const int vs0 = vd0 * kBN + ((vc ^ vswz(vd0)) << 4), vs1 = vd1 * kBN + ((vc ^ vswz(vd1)) << 4);
+  // Tile staging: a K tile is 512 FP8 chunks of 16 bytes (64 keys x 8) and a V^T tile 512
+  // chunks (128 d-rows x 4); each thread owns chunk `tid` of both.  Each group writes its half
+  // during its own matrix-core phase, when its VALU is otherwise idle.
+  const int kr = tid >> 3, kc = tid & 7;                   // key row, 16-byte column
+  const int vd = tid >> 2, vc = tid & 3;                   // d row, 16-byte column
+  const int kw = krow_of_key(kr) * kKPitch + 32 * kc;
+  const int vw = vd * kVPitch + 16 * vc;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (int64_t)bh * N * kD, (uint32_t)N * kD);
-  const uint32_t ko0 = kr0 * kD + kc * 16, ko1 = kr1 * kD + kc * 16;
-  const uint8_t* Vg = a.vt + (int64_t)bh * kD * a.ldv;
-  const uint8_t* vg0 = Vg + (int64_t)vd0 * a.ldv + vc * 16;
-  const uint8_t* vg1 = Vg + (int64_t)vd1 * a.ldv + vc * 16;
-  uint4 kx0, kx1, vx0, vx1;
-#define KQ_GLOAD(k0)                                                 \
-  {                                                                  \
-    kx0 = bload16(krs, (uint32_t)(k0) * kD + ko0);                   \
-    kx1 = bload16(krs, (uint32_t)(k0) * kD + ko1);                   \
-    vx0 = *reinterpret_cast<const uint4*>(vg0 + (k0));               \
-    vx1 = *reinterpret_cast<const uint4*>(vg1 + (k0));               \
-  }
-#define KQ_LSTORE(buf)                                                                   \
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(a.vt + (int64_t)bh * kD * a.ldv, (uint32_t)(kD * a.ldv));
+  const uint32_t ko = kr * kD + kc * 16;
+  const uint32_t vo = (uint32_t)(vd * a.ldv + vc * 16);
+  uint4 kx, vx;
+#define KQ_STAGE_K(buf)                                                                  \
   {                                                                                      \
-    uint8_t* kb_ = Ks[buf];                                                              \
-    uint2 a_ = e4m3x4_to_bf16(kx0.x), b_ = e4m3x4_to_bf16(kx0.y);                        \
-    uint2 c_ = e4m3x4_to_bf16(kx0.z), d_ = e4m3x4_to_bf16(kx0.w);                        \
-    *reinterpret_cast<uint4*>(kb_ + ks00) = make_uint4(a_.x, a_.y, b_.x, b_.y);          \
-    *reinterpret_cast<uint4*>(kb_ + ks01) = make_uint4(c_.x, c_.y, d_.x, d_.y);          \
-    a_ = e4m3x4_to_bf16(kx1.x); b_ = e4m3x4_to_bf16(kx1.y);                              \
-    c_ = e4m3x4_to_bf16(kx1.z); d_ = e4m3x4_to_bf16(kx1.w);                              \
-    *reinterpret_cast<uint4*>(kb_ + ks10) = make_uint4(a_.x, a_.y, b_.x, b_.y);          \
-    *reinterpret_cast<uint4*>(kb_ + ks11) = make_uint4(c_.x, c_.y, d_.x, d_.y);          \
-    *reinterpret_cast<uint4*>(&Vs[buf][vs0]) = vx0;                                      \
-    *reinterpret_cast<uint4*>(&Vs[buf][vs1]) = vx1;                                      \
+    uint8_t* kb_ = Ks + (buf) * kKStage + kw;                                            \
+    const uint2 a_ = e4m3x4_to_bf16(kx.x), b_ = e4m3x4_to_bf16(kx.y);                    \
+    const uint2 c_ = e4m3x4_to_bf16(kx.z), d_ = e4m3x4_to_bf16(kx.w);                    \
+    *reinterpret_cast<uint4*>(kb_) = make_uint4(a_.x, a_.y, b_.x, b_.y);                 \
+    *reinterpret_cast<uint4*>(kb_ + 16) = make_uint4(c_.x, c_.y, d_.x, d_.y);            \
   }
+#define KQ_STAGE_V(buf) { *reinterpret_cast<uint4*>(Vs + (buf) * kVStage + vw) = vx; }
 
   v16f o[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[c][i] = 0.0f;
-  float m_run = -INFINITY;   // integer-valued running offset M
-  float lsum = 0.0f;         // partial row sum of 448 p over this lane's keys
+  v16f s[2];
+  v8i pop = {0, 0, 0, 0, 0, 0, 0, 0};       // P codes of the previous tile (none before tile 0)
+  int pscale = 127;          // E8M0 scale of this lane group's P block (see the softmax)
+  float m_ref = 0.0f;        // per-row reference offset (integer-valued), set on tile 0
+  float m_top = -INFINITY;   // largest block offset seen (for the row statistics)
+  float lsum = 0.0f;         // partial row sum of 448 p * 2^(M_kb - m_ref) over this lane's keys
   const float c1 = a.c1;
-
   const int ntiles = (N + kBN - 1) / kBN;
-  KQ_GLOAD(0)
-  KQ_LSTORE(0)
+
+  // Ping-pong schedule.  Every wave alternates a matrix-core phase (BMM2 of the previous
+  // tile, BMM1 of the current one, staging of the next tiles) and a VALU phase (softmax of the
+  // current tile).  Group 1 runs half a period behind group 0, so on every SIMD one wave is in
+  // its matrix-core phase while the other is in its VALU phase; workgroup barriers separate
+  // the phases.  Phase 2j: group 0 MFMA(j), group 1 softmax(j-1); phase 2j+1: group 0
+  // softmax(j), group 1 MFMA(j).  K(j) and V(j-1) are read in phases 2j and 2j+1; K(j+1) and
+  // V(j) are written to the other buffers in the same two phases (half by each group) and are
+  // complete before phase 2j+2.  Both groups pass 2 * ntiles + 3 barriers.
+  kx = bload16(krs, ko);                       // K(0), all 512 chunks
+  KQ_STAGE_K(0)
+  *reinterpret_cast<uint4*>(Vs + kVStage + vw) = make_uint4(0, 0, 0, 0);   // "V(-1)" = 0
+  kx = bload16(krs, (uint32_t)kBN * kD + ko);  // K(1): this thread's chunk
+  vx = bload16(vrs, vo);                       // V(0)
   __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const int k0 = j * kBN;
-    if (j + 1 < ntiles) KQ_GLOAD(k0 + kBN)
-
-    // ---- BMM1 (bf16 matrix cores on E4M3 values): S^T tile, 64 keys x 32 queries per wave
-    v16f s[2];
+  if (grp == 1) __syncthreads();
+  for (int j = 0; j <= ntiles; ++j) {
+    // ---------------- matrix-core phase (one straight-line block; at j == 0 the P codes and
+    // the V^T buffer are zero, at j == ntiles the scores are never used)
+    const int cur = j & 1;
+    {
+      // Operand window: the 8 V^T reads of BMM2(j-1) and the first 4 K reads of BMM1(j) go
+      // out first; then every MFMA is issued together with the read four K steps ahead, so the
+      // LDS latency hides behind the matrix cores.  sched_barrier(0) pins this order.
+      const uint8_t* vt_ = Vs + (cur ^ 1) * kVStage + vread;
+      const uint8_t* kt_ = Ks + cur * kKStage + kread;
+#define KQ_KREAD(t) (*reinterpret_cast<const uint4*>(kt_ + ((t) & 1) * 32 * kKPitch + 32 * ((t) >> 1)))
+      uint4 vv[8], kv[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int c = 0; c < 4; ++c) {
+        vv[2 * c] = *reinterpret_cast<const uint4*>(vt_ + c * 32 * kVPitch);
+        vv[2 * c + 1] = *reinterpret_cast<const uint4*>(vt_ + c * 32 * kVPitch + 16);
+      }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-    const uint8_t* kt = Ks[buf];
+      for (int t = 0; t < 4; ++t) kv[t] = KQ_KREAD(t);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+      for (int c = 0; c < 4; ++c) {                     // BMM2(j-1): O^T += V^T · P^T
+        o[c] = mfma_f8_scaled(cat8(vv[2 * c], vv[2 * c + 1]), pop, o[c], pscale);
+        kv[4 + c] = KQ_KREAD(4 + c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {                    // BMM1(j): S^T = K · Q^T, t = 2m + kb
+        const int m = t >> 1, kb = t & 1;
+        s[kb] = mfma_bf16(as_bf16x8(kv[t]), qop[m], m == 0 ? v16f{} : s[kb]);
+        if (t + 8 < 16) kv[t + 8] = KQ_KREAD(t + 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#undef KQ_KREAD
+      // stage K(j+1) and V(j) from registers, then prefetch K(j+2) and V(j+1); past the end
+      // the buffer loads return zeros and the stages they fill are never read
+      KQ_STAGE_K(cur ^ 1)
+      KQ_STAGE_V(cur)
+      kx = bload16(krs, (uint32_t)(j + 2) * kBN * kD + ko);
+      vx = bload16(vrs, vo + (uint32_t)(j + 1) * kBN);
+    }
+    __syncthreads();
+    // ---------------- VALU phase: softmax of tile j
+    if (j < ntiles) {
+      const int k0 = j * kBN;
+      // lane (r, g): s[kb][i] = score of query r against key k0 + 32g + 16kb + i
+      if (k0 + kBN > N) {
+        const int nv_ = N - k0 - 32 * g;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (16 * kb + i >= nv_) s[kb][i] = -INFINITY;
+      }
+      // BMM2's P operand is E4M3 with an E8M0 block scale per 32-key block: block kb holds
+      // the s[kb] values of both lanes of a row (bytes 0-15 / 16-31 of each lane's operand),
+      // and lane group g supplies the scale of block g.  Each block is quantized against its
+      // own integer offset M_kb = ceil(max t over the block) (so p <= 1 and 448 p fits E4M3)
+      // and carries 2^(M_kb - m_ref) as its scale: no accumulator rescale when the running
+      // maximum grows.  Codes differ from full-row ones by exact powers of two, which E4M3
+      // rounding preserves in its normal range.
+      float mx0 = s[0][0], mx1 = s[1][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        mx0 = fmaxf(mx0, s[0][i]);
+        mx1 = fmaxf(mx1, s[1][i]);
+      }
+      mx0 = max_with_partner(mx0);
+      mx1 = max_with_partner(mx1);
+      float mb0 = ceilf(mx0 * c1), mb1 = ceilf(mx1 * c1);
+      if (j == 0) {                    // row reference: the row's offset on the first tile
+        const float mr = fmaxf(mb0, mb1);
+        m_ref = (mr == -INFINITY) ? 0.0f : mr;
+      }
+      if (mx0 == -INFINITY) mb0 = m_ref;             // whole block masked: p = 0 below
+      if (mx1 == -INFINITY) mb1 = m_ref;
+      float d0 = mb0 - m_ref, d1 = mb1 - m_ref;
+      if (__builtin_expect(__any(fmaxf(d0, d1) > 64.0f), 0)) {
+        // keep 2^d far from float32 overflow: move the row reference up, rescale exactly
+        const float up = fmaxf(fmaxf(d0, d1) - 32.0f, 0.0f);
+        const float alpha = __builtin_amdgcn_ldexpf(1.0f, -(int)up);
+        lsum *= alpha;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
+        m_ref += up;
+        d0 -= up;
+        d1 -= up;
+      }
+      d0 = fmaxf(d0, -126.0f);         // weights below 2^-126 of the reference: negligible
+      d1 = fmaxf(d1, -126.0f);
+      m_top = fmaxf(m_top, fmaxf(mb0, mb1));
+      pscale = 127 + (int)(g ? d1 : d0);
+      float part[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kv =
-            *reinterpret_cast<const uint4*>(kt + kbase[kb] + (((2 * m + g) ^ ksw[kb]) << 4));
-        s[kb] = mfma_bf16(as_bf16x8(kv), qop[m], s[kb]);
+        const float bias = kLog2_448 - (kb ? mb1 : mb0);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 0], c1, bias));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 1], c1, bias));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 2], c1, bias));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 3], c1, bias));
+          const float q4 = (p0 + p1) + (p2 + p3);
+          part[kb] = i4 ? part[kb] + q4 : q4;
+          // both halves of the dword are written; the previous codes only stand in for the
+          // untouched half of the first conversion
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[4 * kb + i4], false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+          pop[4 * kb + i4] = wd;
+        }
       }
+      const float part0 = part[0], part1 = part[1];
+      lsum += __builtin_amdgcn_ldexpf(part0, (int)d0) + __builtin_amdgcn_ldexpf(part1, (int)d1);
     }
-    // lane (r, g): s[kb][i] = score of query r against key k0 + 32g + 16kb + i
-    if (k0 + kBN > N) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (k0 + 32 * g + 16 * kb + i >= N) s[kb][i] = -INFINITY;
-    }
-
-    // ---- softmax (float32), integer offset in the exp2 domain
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m_run, ceilf(mx * c1));
-    if (__any(mnew != m_run)) {
-      const float alpha =
-          (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)(m_run - mnew));
-      lsum *= alpha;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
-      m_run = mnew;
-    }
-    const float bias = kLog2_448 - m_run;
-    v8i pop;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 0], c1, bias));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 1], c1, bias));
-        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 2], c1, bias));
-        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 3], c1, bias));
-        lsum += (p0 + p1) + (p2 + p3);
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-        pop[4 * kb + i4] = wd;
-      }
-    }
-
-    // ---- BMM2 (FP8 matrix cores): O^T += V^T · P^T, four 32-row blocks of d
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d = 32 * c + r;
-      const uint8_t* vr = &Vs[buf][d * kBN];
-      const int sw = vswz(d);
-      const uint4 lo = *reinterpret_cast<const uint4*>(vr + (((2 * g) ^ sw) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(vr + (((2 * g + 1) ^ sw) << 4));
-      o[c] = mfma_f8(cat8(lo, hi), pop, o[c]);
-    }
-
-    if (j + 1 < ntiles) KQ_LSTORE(buf ^ 1)
     __syncthreads();
   }
-#undef KQ_GLOAD
-#undef KQ_LSTORE
+  if (grp == 0) __syncthreads();
+#undef KQ_STAGE_K
+#undef KQ_STAGE_V
 
   // ---- epilogue: O = acc * s_v / sum(448 p); lane (r, g) holds d = 32c + 8(i/4) + 4g + i%4
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = lsum + __shfl_xor(lsum, 32);      // sum of 448 p relative to m_ref
   const float scale = a.s_v / ltot;
+  const float m_row = fmaxf(m_top, __shfl_xor(m_top, 32));   // the row's M = ceil(max t)
   if (q < N) {
     float* op = a.o + ((int64_t)bh * N + q) * kD;
 #pragma unroll
@@ -287,7 +341,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fp8_kernel(AttnParams a, int
         *reinterpret_cast<float4*>(op + 32 * c + 8 * i4 + 4 * g) = v;
       }
     if (a.stats != nullptr && g == 0) {
-      float2 st = make_float2(m_run, ltot * (1.0f / 448.0f));
+      // (M, l) with l relative to the row's M
+      float2 st = make_float2(m_row, __builtin_amdgcn_ldexpf(ltot * (1.0f / 448.0f), (int)(m_ref - m_row)));
       *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * N + q) * 2) = st;
     }
   }
