@@ -34,13 +34,47 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="workload number (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="no timing: a plain copy of COPY_BYTES (counter calibration), then 3 "
+                         "steps; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
+COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fp8_kontext1024_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "precision_quantized_attention_amd", "csrc", "attn_fp8.hip")
+
+
+def kernel_sha() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_bytes():
+    """HBM bytes per attention launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_sha") != kernel_sha():
+            return None
+        return int(float(fields["attn_fetch_bytes_per_launch"]) +
+                   float(fields["attn_write_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, target_s):
-    """Time the CPU oracle (as it stands) on a bounded sample: a few heads, a subset of rows."""
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload: the full
+    per-tensor quantization of Q, K, V, then R3 attention for query rows of successive heads
+    until about `target_s` seconds have been spent."""
     import numpy as np
     import torch
     import workloads as W
@@ -48,31 +82,38 @@ def cpu_baseline(cfg, target_s):
     from oracle import pipeline as OP
 
     c = W.config(cfg)
-    bits = [b[:, :1] for b in W.qkv_bits(cfg)]          # one head, full sequence
     pos = W.positions(c) if c.rope else None
     t0 = time.perf_counter()
-    qz = OP.quantize_inputs(*bits, mode=c.mode, positions=pos)
+    qz = OP.quantize_inputs(*W.qkv_bits(cfg), mode=c.mode, positions=pos)
     t_quant = time.perf_counter() - t0
-    rows_done, t_attn = 0, 0.0
-    rng = np.random.default_rng(0)
-    order = rng.permutation(c.N)
-    chunk = 256
-    while t_attn + t_quant < target_s and rows_done < c.N:
-        rows = np.sort(order[rows_done:rows_done + chunk])
-        t0 = time.perf_counter()
-        A.attention_r3(qz.codes["q"], qz.codes["k"], qz.codes["v"], qz.scale["q"][0],
-                       qz.scale["k"][0], qz.scale["v"][0], np.float32(1 / math.sqrt(c.d)),
-                       rows=rows)
-        t_attn += time.perf_counter() - t0
-        rows_done += len(rows)
-    # scale to the metric: attention FLOPs of the sampled rows (4*N*d per row) per second;
-    # the per-tensor quantization of the sampled head is charged pro rata
+    rows_done, heads_done, t_attn = 0, 0, 0.0
+    sm = np.float32(1 / math.sqrt(c.d))
+    for b in range(c.B):
+        for h in range(c.H):
+            if t_attn + t_quant >= target_s:
+                break
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            for r0 in range(0, c.N, 1024):
+                if t_attn + t_quant >= target_s:
+                    break
+                rows = np.arange(r0, min(c.N, r0 + 1024))
+                t0 = time.perf_counter()
+                A.attention_r3(qz.codes["q"][sl], qz.codes["k"][sl], qz.codes["v"][sl],
+                               qz.scale["q"][0], qz.scale["k"][0], qz.scale["v"][0], sm,
+                               rows=rows)
+                t_attn += time.perf_counter() - t0
+                rows_done += len(rows)
+            heads_done += 1
+    # attention FLOPs of the processed rows (4*N*d each) per second; the quantization of the
+    # whole tensors is charged in proportion to the rows processed
+    total_rows = c.B * c.H * c.N
     flops = 4.0 * rows_done * c.N * c.d
-    t = t_attn + t_quant * rows_done / c.N
+    t = t_attn + t_quant * rows_done / total_rows
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
             "kind": "oracle",
-            "sample": f"{c.name}: quantize 1 of {c.B * c.H} heads (all {c.N} tokens) + R3 "
-                      f"attention for {rows_done} query rows of that head; {t:.1f} s of CPU"}
+            "sample": f"{c.name}: FP8 quantization of the full Q, K, V ({t_quant:.1f} s) and R3 "
+                      f"attention for {rows_done} query rows in {heads_done} heads "
+                      f"({t_attn:.1f} s); quantization charged pro rata"}
 
 
 def main():
@@ -92,6 +133,17 @@ def main():
                       positions=W.positions(c) if c.rope else None)
     m.calibrate(q, k, v)                     # offline static calibration, not timed
     stream = torch.cuda.current_stream()
+
+    if args.pmc_workload:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        for _ in range(3):
+            m.forward(q, k, v)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_workload": c.name, "copy_bytes": COPY_BYTES, "steps": 3}))
+        return
 
     for _ in range(args.warmup):
         m.forward(q, k, v)
@@ -147,7 +199,8 @@ def main():
                    "step": "FP8 quantize Q,K,V + fused attention (static scales)"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": traffic_bytes()},
         "pct_fp8_peak_step": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "attention_ms": round(attn_ms, 4),
         "quantize_ms": round(quant_ms, 4),
