@@ -21,10 +21,10 @@
 // probabilities, far below the output tolerance.
 //
 // Work decomposition (CDNA4, wave64): workgroup = 8 waves = 256 query rows of one
-// (batch, head), one workgroup per CU; wave = 32 query rows; key tiles of 64 keys.  Per tile
-// the workgroup stages K (converted to bf16, [64][128]) and V^T (FP8, [128][64]) in LDS,
-// double buffered.  The two waves sharing a SIMD run in ping-pong: while one issues matrix-core
-// work the other runs its softmax on the VALU (see the schedule in the kernel).  Both products are computed transposed so each lane owns one query row:
+// (batch, head), one workgroup per CU, two waves per SIMD; wave = 32 query rows; key tiles of
+// 64 keys.  Per tile the workgroup stages K (converted to bf16, [64][128]) and V^T (FP8,
+// [128][64]) in LDS, double buffered.  Both products are computed transposed so each lane
+// owns one query row:
 //   S^T (keys x queries) = K · Q^T      A = K rows from LDS, B = Q (registers, loaded once)
 //   O^T (d x queries)   += V^T · P^T    A = V^T rows from LDS, B = P (registers)
 // so the S accumulator of lane (r, g) holds 32 scores of query r, which is exactly the B
@@ -34,6 +34,15 @@
 // keys 32g .. 32g + 31 of the tile; V^T then supplies them as one contiguous 32-byte run.
 // LDS rows are padded by 16 bytes, which spreads the operand reads of any 8 (or 16)
 // consecutive lanes over distinct 16-byte bank slots.
+//
+// Schedule.  A single wave issues at most one VALU instruction every ~6-7 cycles (exp and the
+// FP8 conversion take two and three issue slots), so the softmax of one tile costs a wave
+// about as long as its 20 matrix-core instructions keep the matrix pipe busy; two waves per
+// SIMD that each interleave the two keep both units busy.  Each step j of a wave therefore
+// issues, in one straight-line block, the matrix-core work of its neighbours — BMM2 of tile
+// j-1 and BMM1 of tile j+1 — with the softmax of tile j slotted between the MFMAs
+// (sched_barrier pins the interleaving), and stages the next tiles; one workgroup barrier
+// per step.
 
 #include "kq_launch.h"
 
@@ -50,7 +59,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
-constexpr int kWaves = 8;                   // two groups of four waves, one wave per SIMD each
+constexpr int kWaves = 8;                   // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;            // query rows per workgroup (32 per wave)
 constexpr int kBN = 64;                     // keys per tile
@@ -59,6 +68,8 @@ constexpr int kVPitch = kBN + 16;           // FP8 V^T row in LDS + 16 bytes of 
 constexpr int kKStage = kBN * kKPitch;      // 17408 bytes
 constexpr int kVStage = kD * kVPitch;       // 10240 bytes
 constexpr float kLog2_448 = 8.807354922057604f;
+
+#define KQ_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Buffer resource over `bytes` bytes from `base`: loads past the end return zeros (the
 // hardware range check), which pads the last key tile and the last query block.
@@ -114,6 +125,178 @@ __device__ __forceinline__ int krow_of_key(int kappa) {
   return 32 * ((kappa >> 4) & 1) + 8 * ((kappa >> 2) & 3) + 4 * ((kappa >> 5) & 1) + (kappa & 3);
 }
 
+// Per-thread constants of a workgroup.
+struct Geo {
+  __amdgpu_buffer_rsrc_t krs, vrs;   // K rows [N][128], V^T rows [128][ldv] of this (b, h)
+  uint32_t ko, vo;                   // this thread's staging chunk in tile 0
+  int kw, vw;                        // its LDS destination within a stage
+  int kread, vread;                  // this lane's operand read bases within a stage
+  int n, g;
+  float c1;
+};
+
+// Stage K(tile) (FP8 codes in kx, converted to bf16) and V^T(tile) (vx) into buffer `buf`.
+__device__ __forceinline__ void stage_k(uint8_t* Ks, int buf, const Geo& G, uint4 kx) {
+  uint8_t* kb = Ks + buf * kKStage + G.kw;
+  const uint2 a = e4m3x4_to_bf16(kx.x), b = e4m3x4_to_bf16(kx.y);
+  const uint2 c = e4m3x4_to_bf16(kx.z), d = e4m3x4_to_bf16(kx.w);
+  *reinterpret_cast<uint4*>(kb) = make_uint4(a.x, a.y, b.x, b.y);
+  *reinterpret_cast<uint4*>(kb + 16) = make_uint4(c.x, c.y, d.x, d.y);
+}
+__device__ __forceinline__ void stage_v(uint8_t* Vs, int buf, const Geo& G, uint4 vx) {
+  *reinterpret_cast<uint4*>(Vs + buf * kVStage + G.vw) = vx;
+}
+
+__device__ __forceinline__ uint4 kread(const uint8_t* kt, int t) {
+  return *reinterpret_cast<const uint4*>(kt + (t & 1) * 32 * kKPitch + 32 * (t >> 1));
+}
+
+// Sets the scores of keys >= N to -inf; lane (r, g): s[kb][i] = key k0 + 32g + 16kb + i.
+__device__ __forceinline__ void mask_tail(v16f (&s)[2], int k0, const Geo& G) {
+  const int nv = G.n - k0 - 32 * G.g;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (16 * kb + i >= nv) s[kb][i] = -INFINITY;
+}
+
+// BMM1 of the tile staged in buffer `buf`, without interleaved work (prologue only).
+__device__ __forceinline__ void bmm1_plain(v16f (&s)[2], const uint8_t* Ks, int buf,
+                                           const Geo& G, const v8bf (&qop)[8]) {
+  const uint8_t* kt = Ks + buf * kKStage + G.kread;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int m = t >> 1, kb = t & 1;
+    s[kb] = mfma_bf16(as_bf16x8(kread(kt, t)), qop[m], m == 0 ? v16f{} : s[kb]);
+  }
+}
+
+// One pipelined step for tile j of a wave:
+//   sc   scores of tile j (in), consumed here;      sn  scores of tile j+1 (out)
+//   pp   P codes of tile j-1 (in, with pscale);     pn  P codes of tile j (out, pscale updated)
+// LDS on entry: K(j+1) in Ks[(j+1)&1], V^T(j-1) in Vs[(j+1)&1]; kx/vx hold K(j+2)/V^T(j).
+// On exit (after the barrier): K(j+2) in Ks[j&1], V^T(j) in Vs[j&1]; kx/vx hold K(j+3)/V^T(j+1).
+template <bool kLast>
+__device__ __forceinline__ void step(int j, v16f (&sc)[2], v16f (&sn)[2], const v8i& pp,
+                                     v8i& pn, int& pscale, v16f (&o)[4], float& m_ref,
+                                     float& m_top, float& lsum, uint4& kx, uint4& vx,
+                                     const v8bf (&qop)[8], uint8_t* Ks, uint8_t* Vs,
+                                     const Geo& G) {
+  const int rb = (j + 1) & 1, wb = j & 1;
+  const uint8_t* vt = Vs + rb * kVStage + G.vread;
+  const uint8_t* kt = Ks + rb * kKStage + G.kread;
+  const float c1 = G.c1;
+
+  // operand reads for the first products
+  uint4 vv[8], kv[16];
+  vv[0] = *reinterpret_cast<const uint4*>(vt);
+  vv[1] = *reinterpret_cast<const uint4*>(vt + 16);
+  vv[2] = *reinterpret_cast<const uint4*>(vt + 32 * kVPitch);
+  vv[3] = *reinterpret_cast<const uint4*>(vt + 32 * kVPitch + 16);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) kv[t] = kread(kt, t);
+  // staging of K(j+2) and V^T(j) into the buffers step j-1 finished reading, then the fetch of
+  // K(j+3) and V^T(j+1) (past the end the loads return zeros and nothing reads the stages)
+  stage_k(Ks, wb, G, kx);
+  stage_v(Vs, wb, G, vx);
+  kx = bload16(G.krs, (uint32_t)(j + 3) * kBN * kD + G.ko);
+  vx = bload16(G.vrs, G.vo + (uint32_t)(j + 1) * kBN);
+  if (kLast) mask_tail(sc, j * kBN, G);
+  KQ_FENCE();
+
+  // ---- BMM2(j-1): O^T += V^T · P^T, with the block maxima of tile j in between
+  float mx0 = fmaxf(sc[0][0], sc[0][1]), mx1 = fmaxf(sc[1][0], sc[1][1]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    o[c] = mfma_f8_scaled(cat8(vv[2 * c], vv[2 * c + 1]), pp, o[c], pscale);
+    if (c < 2) {
+      vv[2 * c + 4] = *reinterpret_cast<const uint4*>(vt + (c + 2) * 32 * kVPitch);
+      vv[2 * c + 5] = *reinterpret_cast<const uint4*>(vt + (c + 2) * 32 * kVPitch + 16);
+    }
+    kv[4 + c] = kread(kt, 4 + c);
+    // 14 remaining values per block: elements 2 .. 15, in 4 chunks
+    const int i0 = 2 + 4 * c - (c == 3 ? 2 : 0);
+    if (c < 3) {
+      mx0 = fmaxf(fmaxf(mx0, sc[0][i0]), sc[0][i0 + 1]);
+      mx0 = fmaxf(fmaxf(mx0, sc[0][i0 + 2]), sc[0][i0 + 3]);
+      mx1 = fmaxf(fmaxf(mx1, sc[1][i0]), sc[1][i0 + 1]);
+      mx1 = fmaxf(fmaxf(mx1, sc[1][i0 + 2]), sc[1][i0 + 3]);
+    } else {
+      mx0 = fmaxf(fmaxf(mx0, sc[0][14]), sc[0][15]);
+      mx1 = fmaxf(fmaxf(mx1, sc[1][14]), sc[1][15]);
+      mx0 = max_with_partner(mx0);
+      mx1 = max_with_partner(mx1);
+    }
+    KQ_FENCE();
+  }
+  // Per-(row, block) offsets.  BMM2's P operand is E4M3 with an E8M0 block scale per 32-key
+  // block: block kb holds the sc[kb] values of both lanes of a row (bytes 0-15 / 16-31 of each
+  // lane's operand), and lane group g supplies the scale of block g.  Each block is quantized
+  // against its own integer offset M_kb = ceil(max t over the block) (so p <= 1 and 448 p fits
+  // E4M3) and carries 2^(M_kb - m_ref) as its scale: no accumulator rescale when the running
+  // maximum grows.  Codes differ from full-row ones by exact powers of two, which E4M3
+  // rounding preserves in its normal range.
+  float mb0 = ceilf(mx0 * c1), mb1 = ceilf(mx1 * c1);
+  if (kLast) {                                   // a fully masked block: p = 0 below
+    if (mx0 == -INFINITY) mb0 = m_ref;
+    if (mx1 == -INFINITY) mb1 = m_ref;
+  }
+  const float bias0 = kLog2_448 - mb0, bias1 = kLog2_448 - mb1;
+
+  // ---- BMM1(j+1): S^T = K · Q^T (t = 2m + kb), with exp2 / E4M3 / row sums of tile j:
+  // slot t handles values 2t, 2t+1 of the 32 (block t/8)
+  float part0 = 0.0f, part1 = 0.0f, pair = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int m = t >> 1, kb = t & 1;
+    sn[kb] = mfma_bf16(as_bf16x8(kv[t]), qop[m], m == 0 ? v16f{} : sn[kb]);
+    if (t + 8 < 16) kv[t + 8] = kread(kt, t + 8);
+    {
+      const int blk = t >> 3, i = 2 * (t & 7);
+      const float bias = blk ? bias1 : bias0;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][i], c1, bias));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][i + 1], c1, bias));
+      const int w = 4 * blk + (i >> 2);
+      if ((i & 2) == 0) {
+        pn[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pp[w], false);
+        pair = p0 + p1;
+      } else {
+        pn[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pn[w], true);
+        const float q4 = pair + (p0 + p1);
+        if (blk) part1 = (i == 2) ? q4 : part1 + q4;
+        else part0 = (i == 2) ? q4 : part0 + q4;
+      }
+    }
+    KQ_FENCE();
+  }
+
+  float d0 = fmaxf(mb0 - m_ref, -126.0f);       // weights below 2^-126 of the reference:
+  float d1 = fmaxf(mb1 - m_ref, -126.0f);       // negligible
+  m_top = fmaxf(m_top, fmaxf(mb0, mb1));
+  const float lsum_in = lsum;
+  lsum += __builtin_amdgcn_ldexpf(part0, (int)d0) + __builtin_amdgcn_ldexpf(part1, (int)d1);
+  // The codes and sums are consumed only by the next step; this empty use keeps them in the
+  // slots above instead of letting the compiler sink them past the branch and the barrier.
+  asm volatile("" ::"v"(pn), "v"(lsum));
+  if (__builtin_expect(__any(fmaxf(d0, d1) > 64.0f), 0)) {
+    // keep 2^d far from float32 overflow: move the row reference up, rescale exactly
+    const float up = fmaxf(fmaxf(d0, d1) - 32.0f, 0.0f);
+    const float alpha = __builtin_amdgcn_ldexpf(1.0f, -(int)up);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
+    m_ref += up;
+    d0 = fmaxf(d0 - up, -126.0f);
+    d1 = fmaxf(d1 - up, -126.0f);
+    lsum = lsum_in * alpha + __builtin_amdgcn_ldexpf(part0, (int)d0) +
+           __builtin_amdgcn_ldexpf(part1, (int)d1);
+  }
+  pscale = 127 + (int)(G.g ? d1 : d0);
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int nqb) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * kKStage];   // bf16 K tiles
   __shared__ __attribute__((aligned(16))) uint8_t Vs[2 * kVStage];   // FP8 V^T tiles
@@ -130,7 +313,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   const int qb = logical - bh * nqb;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, g = l >> 5;
-  const int grp = w >> 2;                   // 0: waves 0-3, 1: waves 4-7 (one per SIMD each)
   const int N = a.n;
   const int q = qb * kBM + w * 32 + r;
 
@@ -148,183 +330,90 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     }
   }
 
-  // Operand read bases (bytes within a stage); block kb / step m / d-block c are immediates.
-  const int kread = r * kKPitch + 16 * g;
-  const int vread = r * kVPitch + 32 * g;
-
   // Tile staging: a K tile is 512 FP8 chunks of 16 bytes (64 keys x 8) and a V^T tile 512
-  // chunks (128 d-rows x 4); each thread owns chunk `tid` of both.  Each group writes its half
-  // during its own matrix-core phase, when its VALU is otherwise idle.
-  const int kr = tid >> 3, kc = tid & 7;                   // key row, 16-byte column
-  const int vd = tid >> 2, vc = tid & 3;                   // d row, 16-byte column
-  const int kw = krow_of_key(kr) * kKPitch + 32 * kc;
-  const int vw = vd * kVPitch + 16 * vc;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (int64_t)bh * N * kD, (uint32_t)N * kD);
-  const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc(a.vt + (int64_t)bh * kD * a.ldv, (uint32_t)(kD * a.ldv));
-  const uint32_t ko = kr * kD + kc * 16;
-  const uint32_t vo = (uint32_t)(vd * a.ldv + vc * 16);
-  uint4 kx, vx;
-#define KQ_STAGE_K(buf)                                                                  \
-  {                                                                                      \
-    uint8_t* kb_ = Ks + (buf) * kKStage + kw;                                            \
-    const uint2 a_ = e4m3x4_to_bf16(kx.x), b_ = e4m3x4_to_bf16(kx.y);                    \
-    const uint2 c_ = e4m3x4_to_bf16(kx.z), d_ = e4m3x4_to_bf16(kx.w);                    \
-    *reinterpret_cast<uint4*>(kb_) = make_uint4(a_.x, a_.y, b_.x, b_.y);                 \
-    *reinterpret_cast<uint4*>(kb_ + 16) = make_uint4(c_.x, c_.y, d_.x, d_.y);            \
+  // chunks (128 d-rows x 4); each thread owns chunk `tid` of both.
+  Geo G;
+  {
+    const int kr = tid >> 3, kc = tid & 7;                 // key row, 16-byte column
+    const int vd = tid >> 2, vc = tid & 3;                 // d row, 16-byte column
+    G.kw = krow_of_key(kr) * kKPitch + 32 * kc;
+    G.vw = vd * kVPitch + 16 * vc;
+    G.krs = make_rsrc(a.k + (int64_t)bh * N * kD, (uint32_t)N * kD);
+    G.vrs = make_rsrc(a.vt + (int64_t)bh * kD * a.ldv, (uint32_t)(kD * a.ldv));
+    G.ko = kr * kD + kc * 16;
+    G.vo = (uint32_t)(vd * a.ldv + vc * 16);
+    G.kread = r * kKPitch + 16 * g;
+    G.vread = r * kVPitch + 32 * g;
+    G.n = N;
+    G.g = g;
+    G.c1 = a.c1;
   }
-#define KQ_STAGE_V(buf) { *reinterpret_cast<uint4*>(Vs + (buf) * kVStage + vw) = vx; }
 
   v16f o[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[c][i] = 0.0f;
-  v16f s[2];
-  v8i pop = {0, 0, 0, 0, 0, 0, 0, 0};       // P codes of the previous tile (none before tile 0)
-  int pscale = 127;          // E8M0 scale of this lane group's P block (see the softmax)
-  float m_ref = 0.0f;        // per-row reference offset (integer-valued), set on tile 0
+  v16f sA[2], sB[2];
+  v8i pA = {0, 0, 0, 0, 0, 0, 0, 0}, pB = pA;   // P codes; "tile -1" has none
+  int pscale = 127;
+  float m_ref = 0.0f;        // per-row reference offset (integer-valued), from tile 0
   float m_top = -INFINITY;   // largest block offset seen (for the row statistics)
   float lsum = 0.0f;         // partial row sum of 448 p * 2^(M_kb - m_ref) over this lane's keys
-  const float c1 = a.c1;
   const int ntiles = (N + kBN - 1) / kBN;
+  const int nfull = ntiles - 1;                  // steps before the (masked) last one
 
-  // Ping-pong schedule.  Every wave alternates a matrix-core phase (BMM2 of the previous
-  // tile, BMM1 of the current one, staging of the next tiles) and a VALU phase (softmax of the
-  // current tile).  Group 1 runs half a period behind group 0, so on every SIMD one wave is in
-  // its matrix-core phase while the other is in its VALU phase; workgroup barriers separate
-  // the phases.  Phase 2j: group 0 MFMA(j), group 1 softmax(j-1); phase 2j+1: group 0
-  // softmax(j), group 1 MFMA(j).  K(j) and V(j-1) are read in phases 2j and 2j+1; K(j+1) and
-  // V(j) are written to the other buffers in the same two phases (half by each group) and are
-  // complete before phase 2j+2.  Both groups pass 2 * ntiles + 3 barriers.
-  kx = bload16(krs, ko);                       // K(0), all 512 chunks
-  KQ_STAGE_K(0)
-  *reinterpret_cast<uint4*>(Vs + kVStage + vw) = make_uint4(0, 0, 0, 0);   // "V(-1)" = 0
-  kx = bload16(krs, (uint32_t)kBN * kD + ko);  // K(1): this thread's chunk
-  vx = bload16(vrs, vo);                       // V(0)
+  // Prologue: K(0) staged and multiplied (scores of tile 0 land in sA, or in sB when the
+  // number of full steps is odd, so that the paired loop below always starts from sA);
+  // K(1) staged, V^T(-1) = 0; kx/vx then hold K(2)/V^T(0).
+  uint4 kx = bload16(G.krs, G.ko), vx;
+  stage_k(Ks, 0, G, kx);
+  *reinterpret_cast<uint4*>(Vs + kVStage + G.vw) = make_uint4(0, 0, 0, 0);
+  kx = bload16(G.krs, (uint32_t)kBN * kD + G.ko);
   __syncthreads();
-  if (grp == 1) __syncthreads();
-  for (int j = 0; j <= ntiles; ++j) {
-    // ---------------- matrix-core phase (one straight-line block; at j == 0 the P codes and
-    // the V^T buffer are zero, at j == ntiles the scores are never used)
-    const int cur = j & 1;
-    {
-      // Operand window: the 8 V^T reads of BMM2(j-1) and the first 4 K reads of BMM1(j) go
-      // out first; then every MFMA is issued together with the read four K steps ahead, so the
-      // LDS latency hides behind the matrix cores.  sched_barrier(0) pins this order.
-      const uint8_t* vt_ = Vs + (cur ^ 1) * kVStage + vread;
-      const uint8_t* kt_ = Ks + cur * kKStage + kread;
-#define KQ_KREAD(t) (*reinterpret_cast<const uint4*>(kt_ + ((t) & 1) * 32 * kKPitch + 32 * ((t) >> 1)))
-      uint4 vv[8], kv[16];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        vv[2 * c] = *reinterpret_cast<const uint4*>(vt_ + c * 32 * kVPitch);
-        vv[2 * c + 1] = *reinterpret_cast<const uint4*>(vt_ + c * 32 * kVPitch + 16);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) kv[t] = KQ_KREAD(t);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {                     // BMM2(j-1): O^T += V^T · P^T
-        o[c] = mfma_f8_scaled(cat8(vv[2 * c], vv[2 * c + 1]), pop, o[c], pscale);
-        kv[4 + c] = KQ_KREAD(4 + c);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {                    // BMM1(j): S^T = K · Q^T, t = 2m + kb
-        const int m = t >> 1, kb = t & 1;
-        s[kb] = mfma_bf16(as_bf16x8(kv[t]), qop[m], m == 0 ? v16f{} : s[kb]);
-        if (t + 8 < 16) kv[t + 8] = KQ_KREAD(t + 8);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#undef KQ_KREAD
-      // stage K(j+1) and V(j) from registers, then prefetch K(j+2) and V(j+1); past the end
-      // the buffer loads return zeros and the stages they fill are never read
-      KQ_STAGE_K(cur ^ 1)
-      KQ_STAGE_V(cur)
-      kx = bload16(krs, (uint32_t)(j + 2) * kBN * kD + ko);
-      vx = bload16(vrs, vo + (uint32_t)(j + 1) * kBN);
-    }
-    __syncthreads();
-    // ---------------- VALU phase: softmax of tile j
-    if (j < ntiles) {
-      const int k0 = j * kBN;
-      // lane (r, g): s[kb][i] = score of query r against key k0 + 32g + 16kb + i
-      if (k0 + kBN > N) {
-        const int nv_ = N - k0 - 32 * g;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (16 * kb + i >= nv_) s[kb][i] = -INFINITY;
-      }
-      // BMM2's P operand is E4M3 with an E8M0 block scale per 32-key block: block kb holds
-      // the s[kb] values of both lanes of a row (bytes 0-15 / 16-31 of each lane's operand),
-      // and lane group g supplies the scale of block g.  Each block is quantized against its
-      // own integer offset M_kb = ceil(max t over the block) (so p <= 1 and 448 p fits E4M3)
-      // and carries 2^(M_kb - m_ref) as its scale: no accumulator rescale when the running
-      // maximum grows.  Codes differ from full-row ones by exact powers of two, which E4M3
-      // rounding preserves in its normal range.
-      float mx0 = s[0][0], mx1 = s[1][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        mx0 = fmaxf(mx0, s[0][i]);
-        mx1 = fmaxf(mx1, s[1][i]);
-      }
-      mx0 = max_with_partner(mx0);
-      mx1 = max_with_partner(mx1);
-      float mb0 = ceilf(mx0 * c1), mb1 = ceilf(mx1 * c1);
-      if (j == 0) {                    // row reference: the row's offset on the first tile
-        const float mr = fmaxf(mb0, mb1);
-        m_ref = (mr == -INFINITY) ? 0.0f : mr;
-      }
-      if (mx0 == -INFINITY) mb0 = m_ref;             // whole block masked: p = 0 below
-      if (mx1 == -INFINITY) mb1 = m_ref;
-      float d0 = mb0 - m_ref, d1 = mb1 - m_ref;
-      if (__builtin_expect(__any(fmaxf(d0, d1) > 64.0f), 0)) {
-        // keep 2^d far from float32 overflow: move the row reference up, rescale exactly
-        const float up = fmaxf(fmaxf(d0, d1) - 32.0f, 0.0f);
-        const float alpha = __builtin_amdgcn_ldexpf(1.0f, -(int)up);
-        lsum *= alpha;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
-        m_ref += up;
-        d0 -= up;
-        d1 -= up;
-      }
-      d0 = fmaxf(d0, -126.0f);         // weights below 2^-126 of the reference: negligible
-      d1 = fmaxf(d1, -126.0f);
-      m_top = fmaxf(m_top, fmaxf(mb0, mb1));
-      pscale = 127 + (int)(g ? d1 : d0);
-      float part[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const float bias = kLog2_448 - (kb ? mb1 : mb0);
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 0], c1, bias));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 1], c1, bias));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 2], c1, bias));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * i4 + 3], c1, bias));
-          const float q4 = (p0 + p1) + (p2 + p3);
-          part[kb] = i4 ? part[kb] + q4 : q4;
-          // both halves of the dword are written; the previous codes only stand in for the
-          // untouched half of the first conversion
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[4 * kb + i4], false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-          pop[4 * kb + i4] = wd;
-        }
-      }
-      const float part0 = part[0], part1 = part[1];
-      lsum += __builtin_amdgcn_ldexpf(part0, (int)d0) + __builtin_amdgcn_ldexpf(part1, (int)d1);
-    }
-    __syncthreads();
+  {
+    v16f (&s0)[2] = (nfull & 1) ? sB : sA;
+    (void)s0;
   }
-  if (grp == 0) __syncthreads();
-#undef KQ_STAGE_K
-#undef KQ_STAGE_V
+  if (nfull & 1) bmm1_plain(sB, Ks, 0, G, qop);
+  else bmm1_plain(sA, Ks, 0, G, qop);
+  stage_k(Ks, 1, G, kx);
+  kx = bload16(G.krs, (uint32_t)2 * kBN * kD + G.ko);
+  vx = bload16(G.vrs, G.vo);
+  {
+    // row reference m_ref = the row's offset on tile 0
+    v16f (&s0)[2] = (nfull & 1) ? sB : sA;
+    v16f t0[2] = {s0[0], s0[1]};
+    if (ntiles == 1) mask_tail(t0, 0, G);
+    float mx = t0[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, t0[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, t0[1][i]);
+    mx = max_with_partner(mx);
+    m_ref = (mx == -INFINITY) ? 0.0f : ceilf(mx * G.c1);
+  }
+  __syncthreads();
+
+  int j = 0;
+  if (nfull & 1) {
+    step<false>(0, sB, sA, pB, pA, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
+    j = 1;
+  }
+  for (; j < nfull; j += 2) {
+    step<false>(j, sA, sB, pA, pB, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
+    step<false>(j + 1, sB, sA, pB, pA, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
+  }
+  step<true>(nfull, sA, sB, pA, pB, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
+  {
+    // BMM2 of the last tile
+    const uint8_t* vt = Vs + (nfull & 1) * kVStage + G.vread;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      o[c] = mfma_f8_scaled(cat8(*reinterpret_cast<const uint4*>(vt + c * 32 * kVPitch),
+                                 *reinterpret_cast<const uint4*>(vt + c * 32 * kVPitch + 16)),
+                            pB, o[c], pscale);
+  }
 
   // ---- epilogue: O = acc * s_v / sum(448 p); lane (r, g) holds d = 32c + 8(i/4) + 4g + i%4
   const float ltot = lsum + __shfl_xor(lsum, 32);      // sum of 448 p relative to m_ref
