@@ -21,7 +21,8 @@
  *
  * Conventions for every entry point below:
  *   - Pointers named *_dev or documented as device pointers are device memory owned by the
- *     caller; the library allocates nothing, keeps no mutable global state and is reentrant.
+ *     caller; the library allocates nothing and is reentrant.  Its only global state is a
+ *     per-device cache of the compute-unit count (written once, read-only after).
  *   - Device buffers must be 16-byte aligned unless stated otherwise.
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no call synchronizes.
  *     A fault inside a kernel surfaces at the caller's next synchronization.
@@ -34,6 +35,7 @@
 #ifndef KQ_H
 #define KQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -137,6 +139,27 @@ kq_status kq_attn_quant_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t*
                             int v_layout, int B, int H, int N, int d, float s_q, float s_k,
                             float s_v, float sm_scale, float* o_f32, float* row_stats_or_null,
                             hipStream_t stream);
+
+/* Bytes of device workspace kq_attn_quant_fwd_ws uses for this shape on the current device
+ * (0 when the launch fills whole rounds of compute units and needs none).  Same argument
+ * rules as kq_attn_quant_fwd; d must be 128.  Host-only apart from one device-attribute query
+ * per device. */
+kq_status kq_attn_workspace_size(int B, int H, int N, int d, size_t* bytes);
+
+/* kq_attn_quant_fwd with a caller-owned device workspace (16-byte aligned, at least
+ * kq_attn_workspace_size bytes for the same shape and device; NULL runs kq_attn_quant_fwd).
+ * The attention of one 256-row query block runs on one compute unit; when the query blocks
+ * leave the last round of the device's compute units partly idle, each block of that round is
+ * split along the keys into consecutive ranges that run on the idle units, and a second kernel
+ * merges their partial results (accumulator, row sum and integer row offset per range) by the
+ * same exact power-of-two rescaling the online softmax uses.  The outputs equal
+ * kq_attn_quant_fwd's up to float32 summation order.  A workspace smaller than required is
+ * KQ_ERR_INVALID_ARG.  Two calls sharing a workspace must be ordered (same stream). */
+kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                               int v_layout, int B, int H, int N, int d, float s_q, float s_k,
+                               float s_v, float sm_scale, float* o_f32,
+                               float* row_stats_or_null, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ import numpy as np
 __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSED",
            "kq_status_string", "kq_vt_ld", "kq_fp8_scales_from_amax", "kq_rope3_table",
            "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
-           "kq_attn_quant_fwd"]
+           "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_LAYOUT_ROWS = 0
@@ -52,6 +52,9 @@ _SIGNATURES = {
     "kq_quantize_fp4_block": ([_P, _I64, _I, _P, _P, _P, _P, _F, ctypes.POINTER(_Rope3), _P],
                               _I),
     "kq_attn_quant_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P], _I),
+    "kq_attn_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], _I),
+    "kq_attn_quant_fwd_ws": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P,
+                              ctypes.c_size_t, _P], _I),
 }
 
 
@@ -206,3 +209,33 @@ def kq_attn_quant_fwd(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale:
         v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
         _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"),
         _stream(stream)), "kq_attn_quant_fwd")
+
+
+def kq_attn_workspace_size(B: int, H: int, N: int, d: int = 128) -> int:
+    """Bytes of device workspace kq_attn_quant_fwd_ws uses for this shape on the current
+    device (0: none needed)."""
+    n = ctypes.c_size_t(0)
+    _check(load().kq_attn_workspace_size(B, H, N, d, ctypes.byref(n)), "kq_attn_workspace_size")
+    return int(n.value)
+
+
+def kq_attn_quant_fwd_ws(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float, o,
+                         workspace, row_stats=None, v_layout: int = KQ_LAYOUT_TRANSPOSED,
+                         stream=None):
+    """kq_attn_quant_fwd with a device workspace (uint8 tensor of at least
+    kq_attn_workspace_size bytes, or None) for the key split of the last round."""
+    import torch
+    B, H, N, d = q8.shape
+    if tuple(k8.shape) != (B, H, N, d) or tuple(o.shape) != (B, H, N, d):
+        raise KQError("k8 and o must match q8's shape")
+    if v_layout == KQ_LAYOUT_TRANSPOSED and v8t.numel() != B * H * d * kq_vt_ld(N):
+        raise KQError("v8t must be [B*H, d, kq_vt_ld(N)]")
+    if row_stats is not None and row_stats.numel() != B * H * N * 2:
+        raise KQError("row_stats must be [B, H, N, 2]")
+    ws = _opt(workspace, torch.uint8, "workspace")
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(load().kq_attn_quant_fwd_ws(
+        _dev(q8, torch.uint8, "q8"), _dev(k8, torch.uint8, "k8"), _dev(v8t, torch.uint8, "v8"),
+        v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
+        _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"), ws, nbytes,
+        _stream(stream)), "kq_attn_quant_fwd_ws")

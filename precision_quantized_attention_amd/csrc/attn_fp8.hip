@@ -62,6 +62,7 @@ constexpr int kD = 128;
 constexpr int kWaves = 8;                   // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;            // query rows per workgroup (32 per wave)
+static_assert(kBM == kAttnRowsPerBlock, "workspace layout assumes 256-row query blocks");
 constexpr int kBN = 64;                     // keys per tile
 constexpr int kKPitch = kD * 2 + 16;        // bf16 K row in LDS + 16 bytes of padding
 constexpr int kVPitch = kBN + 16;           // FP8 V^T row in LDS + 16 bytes of padding
@@ -128,10 +129,11 @@ __device__ __forceinline__ int krow_of_key(int kappa) {
 // Per-thread constants of a workgroup.
 struct Geo {
   __amdgpu_buffer_rsrc_t krs, vrs;   // K rows [N][128], V^T rows [128][ldv] of this (b, h)
-  uint32_t ko, vo;                   // this thread's staging chunk in tile 0
+  uint32_t ko, vo;                   // this thread's staging chunk in the first tile
   int kw, vw;                        // its LDS destination within a stage
   int kread, vread;                  // this lane's operand read bases within a stage
   int n, g;
+  int kbase;                         // first key of the workgroup's key range
   float c1;
 };
 
@@ -202,7 +204,7 @@ __device__ __forceinline__ void step(int j, v16f (&sc)[2], v16f (&sn)[2], const 
   stage_v(Vs, wb, G, vx);
   kx = bload16(G.krs, (uint32_t)(j + 3) * kBN * kD + G.ko);
   vx = bload16(G.vrs, G.vo + (uint32_t)(j + 1) * kBN);
-  if (kLast) mask_tail(sc, j * kBN, G);
+  if (kLast) mask_tail(sc, G.kbase + j * kBN, G);
   KQ_FENCE();
 
   // ---- BMM2(j-1): O^T += V^T · P^T, with the block maxima of tile j in between
@@ -301,19 +303,32 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * kKStage];   // bf16 K tiles
   __shared__ __attribute__((aligned(16))) uint8_t Vs[2 * kVStage];   // FP8 V^T tiles
 
-  // XCD-aware order: consecutive dispatch slots go round-robin over the 8 XCDs, so give each
-  // XCD a contiguous range of (head, query-block) pairs and keep a head's K/V in one L2.
-  const int bid = blockIdx.x, total = gridDim.x;
-  const int xcd = bid & 7, local = bid >> 3, per = total >> 3, rem = total & 7;
-  const int logical = (xcd < rem) ? xcd * (per + 1) + local
-                                  : rem * (per + 1) + (xcd - rem) * per + local;
-  // (the integer division runs on the vector unit; readfirstlane returns the values to scalar
-  // registers so the buffer descriptors below stay scalar)
+  // Work assignment.  Dispatch slots below a.nfull are whole query blocks, in an XCD-aware
+  // order: consecutive slots go round-robin over the 8 XCDs, so each XCD gets a contiguous
+  // range of (head, query-block) pairs and keeps a head's K/V in its own L2.  The slots after
+  // them (dispatched last) are key ranges of the remaining query blocks.
+  // (integer divisions run on the vector unit; readfirstlane returns the uniform results to
+  // scalar registers so the buffer descriptors below stay scalar)
+  const int N = a.n;
+  const int ntiles_all = (N + kBN - 1) / kBN;
+  const int bid = blockIdx.x;
+  int logical, part = -1, t_begin = 0, t_end = ntiles_all;
+  if (bid < a.nfull) {
+    const int total = a.nfull;
+    const int xcd = bid & 7, local = bid >> 3, per = total >> 3, rm = total & 7;
+    logical = (xcd < rm) ? xcd * (per + 1) + local : rm * (per + 1) + (xcd - rm) * per + local;
+  } else {
+    part = bid - a.nfull;
+    const int blk = __builtin_amdgcn_readfirstlane(part / a.split);
+    const int chunk = part - blk * a.split;
+    logical = a.nfull + blk;
+    t_begin = __builtin_amdgcn_readfirstlane(chunk * ntiles_all / a.split);
+    t_end = __builtin_amdgcn_readfirstlane((chunk + 1) * ntiles_all / a.split);
+  }
   const int bh = __builtin_amdgcn_readfirstlane(logical / nqb);
   const int qb = logical - bh * nqb;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, g = l >> 5;
-  const int N = a.n;
   const int q = qb * kBM + w * 32 + r;
 
   // Q operand (bf16 values of the E4M3 codes): step m covers d = 16m .. 16m + 15; lane (r, g)
@@ -340,12 +355,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     G.vw = vd * kVPitch + 16 * vc;
     G.krs = make_rsrc(a.k + (int64_t)bh * N * kD, (uint32_t)N * kD);
     G.vrs = make_rsrc(a.vt + (int64_t)bh * kD * a.ldv, (uint32_t)(kD * a.ldv));
-    G.ko = kr * kD + kc * 16;
-    G.vo = (uint32_t)(vd * a.ldv + vc * 16);
+    G.ko = (uint32_t)t_begin * kBN * kD + kr * kD + kc * 16;
+    G.vo = (uint32_t)(vd * a.ldv + vc * 16 + t_begin * kBN);
     G.kread = r * kKPitch + 16 * g;
     G.vread = r * kVPitch + 32 * g;
     G.n = N;
     G.g = g;
+    G.kbase = t_begin * kBN;
     G.c1 = a.c1;
   }
 
@@ -360,7 +376,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   float m_ref = 0.0f;        // per-row reference offset (integer-valued), from tile 0
   float m_top = -INFINITY;   // largest block offset seen (for the row statistics)
   float lsum = 0.0f;         // partial row sum of 448 p * 2^(M_kb - m_ref) over this lane's keys
-  const int ntiles = (N + kBN - 1) / kBN;
+  const int ntiles = t_end - t_begin;            // tiles of this workgroup's key range
   const int nfull = ntiles - 1;                  // steps before the (masked) last one
 
   // Prologue: K(0) staged and multiplied (scores of tile 0 land in sA, or in sB when the
@@ -371,10 +387,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   *reinterpret_cast<uint4*>(Vs + kVStage + G.vw) = make_uint4(0, 0, 0, 0);
   kx = bload16(G.krs, (uint32_t)kBN * kD + G.ko);
   __syncthreads();
-  {
-    v16f (&s0)[2] = (nfull & 1) ? sB : sA;
-    (void)s0;
-  }
   if (nfull & 1) bmm1_plain(sB, Ks, 0, G, qop);
   else bmm1_plain(sA, Ks, 0, G, qop);
   stage_k(Ks, 1, G, kx);
@@ -384,7 +396,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     // row reference m_ref = the row's offset on tile 0
     v16f (&s0)[2] = (nfull & 1) ? sB : sA;
     v16f t0[2] = {s0[0], s0[1]};
-    if (ntiles == 1) mask_tail(t0, 0, G);
+    if (G.kbase + kBN > N) mask_tail(t0, G.kbase, G);
     float mx = t0[0][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, t0[0][i]);
@@ -417,8 +429,24 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
 
   // ---- epilogue: O = acc * s_v / sum(448 p); lane (r, g) holds d = 32c + 8(i/4) + 4g + i%4
   const float ltot = lsum + __shfl_xor(lsum, 32);      // sum of 448 p relative to m_ref
-  const float scale = a.s_v / ltot;
   const float m_row = fmaxf(m_top, __shfl_xor(m_top, 32));   // the row's M = ceil(max t)
+  if (part >= 0) {
+    // partial result of a key range: the unnormalized accumulator and (m_ref, l, M)
+    const int row = w * 32 + r;
+    float* wo = a.ws + ((int64_t)part * kBM + row) * kD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(wo + 32 * c + 8 * i4 + 4 * g) =
+            make_float4(o[c][4 * i4], o[c][4 * i4 + 1], o[c][4 * i4 + 2], o[c][4 * i4 + 3]);
+    if (g == 0) {
+      float* ws = a.ws + (int64_t)a.rem * a.split * kBM * kD + ((int64_t)part * kBM + row) * 4;
+      *reinterpret_cast<float4*>(ws) = make_float4(m_ref, ltot, m_row, 0.0f);
+    }
+    return;
+  }
+  const float scale = a.s_v / ltot;
   if (q < N) {
     float* op = a.o + ((int64_t)bh * N + q) * kD;
 #pragma unroll
@@ -437,12 +465,58 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   }
 }
 
+// Merge of the key-range partials of one query block: with R = max m_ref over the parts,
+// acc = sum acc_s 2^(m_ref_s - R) and l = sum l_s 2^(m_ref_s - R) (exact power-of-two scaling),
+// then O = acc * s_v / l as in the single-pass epilogue.  One thread per (row, 4 columns).
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row_all = gid >> 5, d4 = 4 * (gid & 31);
+  const int blk = row_all / kBM, row = row_all - blk * kBM;
+  if (blk >= a.rem) return;
+  const int logical = a.nfull + blk;
+  const int bh = logical / nqb, qb = logical - bh * nqb;
+  const int q = qb * kBM + row;
+  if (q >= a.n) return;
+  const float4* st = reinterpret_cast<const float4*>(a.ws + (int64_t)a.rem * a.split * kBM * kD) +
+                     (int64_t)blk * a.split * kBM + row;
+  float R = -INFINITY, m_row = -INFINITY;
+  for (int s = 0; s < a.split; ++s) {
+    const float4 v = st[(int64_t)s * kBM];
+    R = fmaxf(R, v.x);
+    m_row = fmaxf(m_row, v.z);
+  }
+  float l = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = 0; s < a.split; ++s) {
+    const float4 v = st[(int64_t)s * kBM];
+    const float f = __builtin_amdgcn_ldexpf(1.0f, (int)(v.x - R));
+    l += v.y * f;
+    const float4 x = *reinterpret_cast<const float4*>(
+        a.ws + (((int64_t)blk * a.split + s) * kBM + row) * kD + d4);
+    acc.x += x.x * f;
+    acc.y += x.y * f;
+    acc.z += x.z * f;
+    acc.w += x.w * f;
+  }
+  const float scale = a.s_v / l;
+  float* op = a.o + ((int64_t)bh * a.n + q) * kD + d4;
+  *reinterpret_cast<float4*>(op) = make_float4(acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale);
+  if (a.stats != nullptr && d4 == 0) {
+    *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * a.n + q) * 2) =
+        make_float2(m_row, __builtin_amdgcn_ldexpf(l * (1.0f / 448.0f), (int)(R - m_row)));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream) {
   const int nqb = (p.n + kBM - 1) / kBM;
-  const int64_t blocks = (int64_t)nqb * p.bh;
+  const int64_t blocks = (int64_t)p.nfull + (int64_t)p.rem * p.split;
   hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.split == 0) return e;
+  const int64_t cblocks = ((int64_t)p.rem * kBM * 32 + 255) / 256;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream, p, nqb);
   return hipGetLastError();
 }
 

@@ -7,6 +7,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -15,6 +18,84 @@ kq_status from_hip(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_HIP; 
 
 constexpr int64_t kVtAlign = 128;
 constexpr int kAxes[3] = {16, 56, 56};
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+struct SplitPlan {
+  int nfull, rem, split;
+};
+
+// Attention workgroups are 256-row query blocks, one per CU at a time.  When the blocks do not
+// fill the last round of the device's CUs, the `rem` blocks of that round are split along the
+// keys into `split` = floor(cus / rem) ranges (at most one per key tile), so the round runs
+// on (nearly) all CUs for 1/split of the time.
+SplitPlan plan_split(int64_t nblocks, int ntiles, int cus) {
+  SplitPlan pl{(int)nblocks, 0, 0};
+  if (cus <= 0) return pl;
+  const int64_t rounds = nblocks / cus, rem = nblocks - rounds * cus;
+  if (rem == 0) return pl;
+  const int split = (int)std::min<int64_t>(cus / rem, ntiles);
+  if (split < 2) return pl;
+  pl.nfull = (int)(rounds * cus);
+  pl.rem = (int)rem;
+  pl.split = split;
+  return pl;
+}
+
+// Validation shared by the attention entry points; fills p (without the split fields).
+kq_status attn_params(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, int v_layout,
+                      int B, int H, int N, int d, float s_q, float s_k, float s_v,
+                      float sm_scale, float* o_f32, float* row_stats_or_null,
+                      kq::AttnParams* p) {
+  if (q8 == nullptr || k8 == nullptr || v8 == nullptr || o_f32 == nullptr) return KQ_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return KQ_ERR_INVALID_ARG;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o_f32, 16))
+    return KQ_ERR_INVALID_ARG;
+  if (row_stats_or_null != nullptr && !aligned(row_stats_or_null, 8)) return KQ_ERR_INVALID_ARG;
+  if (!finite_pos(s_q) || !finite_pos(s_k) || !finite_pos(s_v) || !finite_pos(sm_scale))
+    return KQ_ERR_INVALID_ARG;
+  if (v_layout != KQ_LAYOUT_ROWS && v_layout != KQ_LAYOUT_TRANSPOSED) return KQ_ERR_INVALID_ARG;
+  if (d != 128 || v_layout != KQ_LAYOUT_TRANSPOSED) return KQ_ERR_UNSUPPORTED;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t nqb = ((int64_t)N + kq::kAttnRowsPerBlock - 1) / kq::kAttnRowsPerBlock;
+  // per-(b, h) byte offsets are 32-bit: N * 128 and 128 * kq_vt_ld(N) below 2^31
+  if (bh * nqb > INT32_MAX || kq_vt_ld(N) * 128 >= ((int64_t)1 << 31)) return KQ_ERR_UNSUPPORTED;
+  const double c1 = (double)s_q * (double)s_k * (double)sm_scale * 1.4426950408889634;
+  if (!isfinite(c1) || !isfinite((float)c1) || (float)c1 <= 0.0f) return KQ_ERR_INVALID_ARG;
+  p->q = q8;
+  p->k = k8;
+  p->vt = v8;
+  p->o = o_f32;
+  p->stats = row_stats_or_null;
+  p->bh = (int)bh;
+  p->n = N;
+  p->ldv = kq_vt_ld(N);
+  p->c1 = (float)c1;
+  p->s_v = s_v;
+  p->nfull = (int)(bh * nqb);
+  p->rem = 0;
+  p->split = 0;
+  p->ws = nullptr;
+  return KQ_OK;
+}
+
+SplitPlan attn_plan(int B, int H, int N) {
+  const int64_t nqb = ((int64_t)N + kq::kAttnRowsPerBlock - 1) / kq::kAttnRowsPerBlock;
+  return plan_split((int64_t)B * H * nqb, (N + 63) / 64, device_cus());
+}
 
 }  // namespace
 
@@ -127,31 +208,41 @@ kq_status kq_attn_quant_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t*
                             int v_layout, int B, int H, int N, int d, float s_q, float s_k,
                             float s_v, float sm_scale, float* o_f32, float* row_stats_or_null,
                             hipStream_t stream) {
-  if (q8 == nullptr || k8 == nullptr || v8 == nullptr || o_f32 == nullptr) return KQ_ERR_INVALID_ARG;
-  if (B < 1 || H < 1 || N < 1 || d < 1) return KQ_ERR_INVALID_ARG;
-  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o_f32, 16))
-    return KQ_ERR_INVALID_ARG;
-  if (row_stats_or_null != nullptr && !aligned(row_stats_or_null, 8)) return KQ_ERR_INVALID_ARG;
-  if (!finite_pos(s_q) || !finite_pos(s_k) || !finite_pos(s_v) || !finite_pos(sm_scale))
-    return KQ_ERR_INVALID_ARG;
-  if (v_layout != KQ_LAYOUT_ROWS && v_layout != KQ_LAYOUT_TRANSPOSED) return KQ_ERR_INVALID_ARG;
-  if (d != 128 || v_layout != KQ_LAYOUT_TRANSPOSED) return KQ_ERR_UNSUPPORTED;
-  const int64_t bh = (int64_t)B * H;
-  const int64_t nqb = ((int64_t)N + 127) / 128;
-  if (bh * nqb > INT32_MAX || bh * (int64_t)N * 128 > ((int64_t)1 << 40)) return KQ_ERR_UNSUPPORTED;
-  const double c1 = (double)s_q * (double)s_k * (double)sm_scale * 1.4426950408889634;
-  if (!isfinite(c1) || !isfinite((float)c1) || (float)c1 <= 0.0f) return KQ_ERR_INVALID_ARG;
   kq::AttnParams p;
-  p.q = q8;
-  p.k = k8;
-  p.vt = v8;
-  p.o = o_f32;
-  p.stats = row_stats_or_null;
-  p.bh = (int)bh;
-  p.n = N;
-  p.ldv = kq_vt_ld(N);
-  p.c1 = (float)c1;
-  p.s_v = s_v;
+  const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
+                                   o_f32, row_stats_or_null, &p);
+  if (st != KQ_OK) return st;
+  return from_hip(kq::launch_attn_fp8(p, stream));
+}
+
+kq_status kq_attn_workspace_size(int B, int H, int N, int d, size_t* bytes) {
+  if (bytes == nullptr || B < 1 || H < 1 || N < 1 || d < 1) return KQ_ERR_INVALID_ARG;
+  if (d != 128) return KQ_ERR_UNSUPPORTED;
+  const SplitPlan pl = attn_plan(B, H, N);
+  *bytes = kq::attn_workspace_bytes(pl.rem, pl.split);
+  return KQ_OK;
+}
+
+kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                               int v_layout, int B, int H, int N, int d, float s_q, float s_k,
+                               float s_v, float sm_scale, float* o_f32,
+                               float* row_stats_or_null, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  kq::AttnParams p;
+  const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
+                                   o_f32, row_stats_or_null, &p);
+  if (st != KQ_OK) return st;
+  if (workspace != nullptr && !aligned(workspace, 16)) return KQ_ERR_INVALID_ARG;
+  if (workspace != nullptr) {
+    const SplitPlan pl = attn_plan(B, H, N);
+    if (pl.split > 0) {
+      if (workspace_bytes < kq::attn_workspace_bytes(pl.rem, pl.split)) return KQ_ERR_INVALID_ARG;
+      p.nfull = pl.nfull;
+      p.rem = pl.rem;
+      p.split = pl.split;
+      p.ws = static_cast<float*>(workspace);
+    }
+  }
   return from_hip(kq::launch_attn_fp8(p, stream));
 }
 

@@ -31,7 +31,22 @@ struct AttnParams {
   int64_t ldv;
   float c1;               // s_q * s_k * sm_scale * log2(e), rounded once to float32
   float s_v;
+  // Key split of the last, partial round of query blocks (split == 0: none).  Query blocks
+  // [0, nfull) run whole; each of the `rem` blocks after them runs as `split` workgroups over
+  // consecutive key ranges, writing partial results to `ws`, merged by a second kernel.
+  int nfull;
+  int rem;
+  int split;
+  float* ws;              // [rem * split][256][128] partial acc, then [rem * split][256][4] stats
 };
+
+// Query rows per attention workgroup (the unit of the split).
+constexpr int kAttnRowsPerBlock = 256;
+
+// Bytes of workspace for `rem * split` partial query blocks.
+inline size_t attn_workspace_bytes(int rem, int split) {
+  return (size_t)rem * split * kAttnRowsPerBlock * (128 + 4) * sizeof(float);
+}
 
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream);
 

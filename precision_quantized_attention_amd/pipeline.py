@@ -22,7 +22,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (KQ_LAYOUT_TRANSPOSED, kq_amax_calibrate, kq_attn_quant_fwd,
+from . import (KQ_LAYOUT_TRANSPOSED, kq_amax_calibrate, kq_attn_quant_fwd_ws,
+               kq_attn_workspace_size,
                kq_fp8_scales_from_amax, kq_quantize_fp4_block, kq_quantize_fp8_tensor,
                kq_rope3_table, kq_vt_ld)
 
@@ -60,6 +61,7 @@ class QuantizedSDPA:
             table = torch.from_numpy(kq_rope3_table(positions)).to(self.device)
             self.rope = (table, N)
         self.scales = None            # name -> (s, inv), static after calibrate()
+        self.workspace = None         # attention workspace (allocated on first use)
         self.amax = None
         shape = (B, H, N, d)
         u8 = dict(dtype=torch.uint8, device=self.device)
@@ -114,8 +116,14 @@ class QuantizedSDPA:
 
     def attention(self):
         b = self.buf
-        kq_attn_quant_fwd(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
-                          self.scales["v"][0], self.sm_scale, b.o, row_stats=b.stats)
+        if self.workspace is None:
+            nbytes = kq_attn_workspace_size(self.B, self.H, self.N, self.d)
+            self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+                              if nbytes else False)
+        kq_attn_quant_fwd_ws(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
+                             self.scales["v"][0], self.sm_scale, b.o,
+                             self.workspace if self.workspace is not False else None,
+                             row_stats=b.stats)
         return b.o
 
     def forward(self, q, k, v):

@@ -75,6 +75,19 @@ def test_validation_rejects_before_any_hip_call():
              None) == INVALID
     assert A(odd, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, None) == INVALID
     assert A(fake, fake, fake, 5, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, None) == INVALID
+    W = lib.kq_attn_quant_fwd_ws                 # same checks, then the workspace alignment
+    assert W(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, None, None, fake, 1 << 20,
+             None) == INVALID
+    assert W(fake, fake, fake, 1, 1, 1, 128, 64, 1.0, 1.0, 1.0, 0.1, fake, None, fake, 1 << 20,
+             None) == UNSUPPORTED
+    assert W(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, odd, 1 << 20,
+             None) == INVALID
+    n = ctypes.c_size_t(0)
+    S = lib.kq_attn_workspace_size
+    assert S(1, 1, 128, 128, None) == INVALID
+    assert S(0, 1, 128, 128, ctypes.byref(n)) == INVALID
+    assert S(1, 1, 0, 128, ctypes.byref(n)) == INVALID
+    assert S(1, 1, 128, 64, ctypes.byref(n)) == UNSUPPORTED
 
 
 def test_scale_rule_matches_oracle():

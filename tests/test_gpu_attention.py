@@ -115,6 +115,47 @@ def test_attention_batch_heads_and_fp4_small():
     _compare(o.cpu().numpy(), O, "B2H3 fp4 rope")
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 2, 256), (1, 1, 4096), (1, 3, 8704), (1, 2, 1000),
+                                   (1, 2, 65)])
+def test_attention_key_split_matches_single_pass(B, H, N):
+    """The workspace path splits the query blocks of a partial last round along the keys and
+    merges the parts; it must agree with the single-pass kernel (same codes, float32 order
+    only) and with the oracle on sampled rows."""
+    print(f"key split B={B} H={H} N={N}", flush=True)
+    bits = [W.random_bits(B, H, N, 128, seed=900 + 7 * N + H + t, outliers=True) for t in range(3)]
+    m = QuantizedSDPA(B, H, N, 128, want_stats=True)
+    x = [to_dev(b) for b in bits]
+    m.calibrate(*x)
+    m.quantize(*x)
+    nbytes = kq.kq_attn_workspace_size(B, H, N)
+    print(f"  workspace {nbytes} bytes", flush=True)
+    assert nbytes > 0                  # every shape here leaves the last round partly idle
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = m.buf
+    sc = [m.scales[n][0] for n in "qkv"]
+    o1 = torch.empty_like(b.o)
+    st1 = torch.empty_like(b.stats)
+    kq.kq_attn_quant_fwd(b.q8, b.k8, b.v8t, *sc, m.sm_scale, o1, row_stats=st1)
+    o2 = torch.empty_like(b.o)
+    st2 = torch.empty_like(b.stats)
+    kq.kq_attn_quant_fwd_ws(b.q8, b.k8, b.v8t, *sc, m.sm_scale, o2, ws, row_stats=st2)
+    torch.cuda.synchronize()
+    a1, a2 = o1.cpu().numpy(), o2.cpu().numpy()
+    assert rel_l2(a2, a1) <= 1e-5 and max_abs(a2, a1) <= 1e-4, (rel_l2(a2, a1), max_abs(a2, a1))
+    s1, s2 = st1.cpu().numpy(), st2.cpu().numpy()
+    assert np.array_equal(s1[..., 0], s2[..., 0])
+    assert np.allclose(s1[..., 1], s2[..., 1], rtol=1e-5)
+    with pytest.raises(kq.KQError):            # too small a workspace is rejected
+        kq.kq_attn_quant_fwd_ws(b.q8, b.k8, b.v8t, *sc, m.sm_scale, o2, ws[: nbytes - 16])
+    qz = OP.quantize_inputs(*bits)
+    rows = sample_rows(N, 8, seed=N)
+    hs = [(0, 0), (B - 1, H - 1)]
+    sub = {n: np.stack([qz.codes[n][bb, hh] for bb, hh in hs])[None] for n in "qkv"}
+    O, _, _ = A.attention_r3(sub["q"], sub["k"], sub["v"], qz.scale["q"][0], qz.scale["k"][0],
+                             qz.scale["v"][0], m.sm_scale, rows=rows)
+    _compare(np.stack([a2[bb, hh][rows] for bb, hh in hs]), O[0], f"split B{B} H{H} N{N}")
+
+
 def test_attention_deterministic():
     bits = [b[:, :4] for b in W.qkv_bits(2)]
     m, o1 = _run(bits)
