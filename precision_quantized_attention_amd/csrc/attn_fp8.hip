@@ -35,14 +35,15 @@
 // LDS rows are padded by 16 bytes, which spreads the operand reads of any 8 (or 16)
 // consecutive lanes over distinct 16-byte bank slots.
 //
-// Schedule.  A single wave issues at most one VALU instruction every ~6-7 cycles (exp and the
-// FP8 conversion take two and three issue slots), so the softmax of one tile costs a wave
-// about as long as its 20 matrix-core instructions keep the matrix pipe busy; two waves per
-// SIMD that each interleave the two keep both units busy.  Each step j of a wave therefore
-// issues, in one straight-line block, the matrix-core work of its neighbours — BMM2 of tile
-// j-1 and BMM1 of tile j+1 — with the softmax of tile j slotted between the MFMAs
-// (sched_barrier pins the interleaving), and stages the next tiles; one workgroup barrier
-// per step.
+// Schedule (measured on gfx950).  A single wave issues a VALU instruction about every 6-7
+// cycles (exp2 and the FP8 conversion cost more) and overlaps only part of that work with its
+// own bf16 MFMAs; when both waves of a SIMD mix MFMA and VALU work finely, the older one takes
+// the matrix pipe and the other stalls behind its MFMA issues.  So the two waves of each SIMD
+// alternate roles (ping-pong): one issues the 20 MFMAs of a tile (matrix-core phase, raised
+// priority) with the light VALU work that fits between them — the E4M3 codes and row sums of
+// the previous tile, the block maxima of this one, the staging — while the other runs the
+// exp2 part of its softmax (VALU phase); workgroup barriers separate the phases.
+// sched_barrier pins the interleaving inside the matrix-core phase.
 
 #include "kq_launch.h"
 
@@ -163,108 +164,50 @@ __device__ __forceinline__ void mask_tail(v16f (&s)[2], int k0, const Geo& G) {
       if (16 * kb + i >= nv) s[kb][i] = -INFINITY;
 }
 
-// BMM1 of the tile staged in buffer `buf`, without interleaved work (prologue only).
-__device__ __forceinline__ void bmm1_plain(v16f (&s)[2], const uint8_t* Ks, int buf,
-                                           const Geo& G, const v8bf (&qop)[8]) {
-  const uint8_t* kt = Ks + buf * kKStage + G.kread;
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int m = t >> 1, kb = t & 1;
-    s[kb] = mfma_bf16(as_bf16x8(kread(kt, t)), qop[m], m == 0 ? v16f{} : s[kb]);
-  }
-}
-
-// One pipelined step for tile j of a wave:
-//   sc   scores of tile j (in), consumed here;      sn  scores of tile j+1 (out)
-//   pp   P codes of tile j-1 (in, with pscale);     pn  P codes of tile j (out, pscale updated)
-// LDS on entry: K(j+1) in Ks[(j+1)&1], V^T(j-1) in Vs[(j+1)&1]; kx/vx hold K(j+2)/V^T(j).
-// On exit (after the barrier): K(j+2) in Ks[j&1], V^T(j) in Vs[j&1]; kx/vx hold K(j+3)/V^T(j+1).
-template <bool kLast>
-__device__ __forceinline__ void step(int j, v16f (&sc)[2], v16f (&sn)[2], const v8i& pp,
-                                     v8i& pn, int& pscale, v16f (&o)[4], float& m_ref,
-                                     float& m_top, float& lsum, uint4& kx, uint4& vx,
-                                     const v8bf (&qop)[8], uint8_t* Ks, uint8_t* Vs,
-                                     const Geo& G) {
-  const int rb = (j + 1) & 1, wb = j & 1;
-  const uint8_t* vt = Vs + rb * kVStage + G.vread;
-  const uint8_t* kt = Ks + rb * kKStage + G.kread;
-  const float c1 = G.c1;
-
-  // operand reads for the first products
-  uint4 vv[8], kv[16];
-  vv[0] = *reinterpret_cast<const uint4*>(vt);
-  vv[1] = *reinterpret_cast<const uint4*>(vt + 16);
-  vv[2] = *reinterpret_cast<const uint4*>(vt + 32 * kVPitch);
-  vv[3] = *reinterpret_cast<const uint4*>(vt + 32 * kVPitch + 16);
+// Matrix-core phase j of a wave (see the schedule in the kernel):
+//   BMM1(j): sn = S^T of tile j (K(j) in Ks[j&1]), t = 2m + kb;
+//   in the slots between those MFMAs the float32 448 p of tile j-1 (pv, written by the
+//   previous VALU phase) become the E4M3 codes pop and per-block partial sums, added to lsum
+//   with the block offsets d0p, d1p of tile j-1; slot t handles values 2t, 2t+1 (block t/8);
+//   BMM2(j-1): O^T += V^T(j-1) · P(j-1)^T with the E8M0 block scale pscale (V^T(j-1) in
+//   Vs[(j+1)&1]), with this thread's staging of K(j+1) into Ks[(j+1)&1] and V^T(j) into
+//   Vs[j&1] (from kx/vx) and the block maxima of tile j (mx0, mx1 over keys 32g + 16kb ..,
+//   both lanes of a row; keys past N masked to -inf first) in its slots, then the fetch of
+//   K(j+2) and V^T(j+1).
+// The wave runs this phase at raised priority: its few VALU instructions and the MFMA issues
+// behind them then win the arbitration against the other wave of the SIMD, which is in its
+// VALU phase, and the matrix pipe stays fed.
+__device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv)[2], v8i& pop,
+                                           int pscale, float d0p, float d1p, v16f (&o)[4],
+                                           float& lsum, uint4& kx, uint4& vx, float& mx0,
+                                           float& mx1, const v8bf (&qop)[8], uint8_t* Ks,
+                                           uint8_t* Vs, const Geo& G) {
+  __builtin_amdgcn_s_setprio(1);
+  const int cur = j & 1;
+  const uint8_t* kt = Ks + cur * kKStage + G.kread;
+  const uint8_t* vt = Vs + (cur ^ 1) * kVStage + G.vread;
+  uint4 kv[16], vv[8];
 #pragma unroll
   for (int t = 0; t < 4; ++t) kv[t] = kread(kt, t);
-  // staging of K(j+2) and V^T(j) into the buffers step j-1 finished reading, then the fetch of
-  // K(j+3) and V^T(j+1) (past the end the loads return zeros and nothing reads the stages)
-  stage_k(Ks, wb, G, kx);
-  stage_v(Vs, wb, G, vx);
-  kx = bload16(G.krs, (uint32_t)(j + 3) * kBN * kD + G.ko);
-  vx = bload16(G.vrs, G.vo + (uint32_t)(j + 1) * kBN);
-  if (kLast) mask_tail(sc, G.kbase + j * kBN, G);
   KQ_FENCE();
-
-  // ---- BMM2(j-1): O^T += V^T · P^T, with the block maxima of tile j in between
-  float mx0 = fmaxf(sc[0][0], sc[0][1]), mx1 = fmaxf(sc[1][0], sc[1][1]);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    o[c] = mfma_f8_scaled(cat8(vv[2 * c], vv[2 * c + 1]), pp, o[c], pscale);
-    if (c < 2) {
-      vv[2 * c + 4] = *reinterpret_cast<const uint4*>(vt + (c + 2) * 32 * kVPitch);
-      vv[2 * c + 5] = *reinterpret_cast<const uint4*>(vt + (c + 2) * 32 * kVPitch + 16);
-    }
-    kv[4 + c] = kread(kt, 4 + c);
-    // 14 remaining values per block: elements 2 .. 15, in 4 chunks
-    const int i0 = 2 + 4 * c - (c == 3 ? 2 : 0);
-    if (c < 3) {
-      mx0 = fmaxf(fmaxf(mx0, sc[0][i0]), sc[0][i0 + 1]);
-      mx0 = fmaxf(fmaxf(mx0, sc[0][i0 + 2]), sc[0][i0 + 3]);
-      mx1 = fmaxf(fmaxf(mx1, sc[1][i0]), sc[1][i0 + 1]);
-      mx1 = fmaxf(fmaxf(mx1, sc[1][i0 + 2]), sc[1][i0 + 3]);
-    } else {
-      mx0 = fmaxf(fmaxf(mx0, sc[0][14]), sc[0][15]);
-      mx1 = fmaxf(fmaxf(mx1, sc[1][14]), sc[1][15]);
-      mx0 = max_with_partner(mx0);
-      mx1 = max_with_partner(mx1);
-    }
-    KQ_FENCE();
-  }
-  // Per-(row, block) offsets.  BMM2's P operand is E4M3 with an E8M0 block scale per 32-key
-  // block: block kb holds the sc[kb] values of both lanes of a row (bytes 0-15 / 16-31 of each
-  // lane's operand), and lane group g supplies the scale of block g.  Each block is quantized
-  // against its own integer offset M_kb = ceil(max t over the block) (so p <= 1 and 448 p fits
-  // E4M3) and carries 2^(M_kb - m_ref) as its scale: no accumulator rescale when the running
-  // maximum grows.  Codes differ from full-row ones by exact powers of two, which E4M3
-  // rounding preserves in its normal range.
-  float mb0 = ceilf(mx0 * c1), mb1 = ceilf(mx1 * c1);
-  if (kLast) {                                   // a fully masked block: p = 0 below
-    if (mx0 == -INFINITY) mb0 = m_ref;
-    if (mx1 == -INFINITY) mb1 = m_ref;
-  }
-  const float bias0 = kLog2_448 - mb0, bias1 = kLog2_448 - mb1;
-
-  // ---- BMM1(j+1): S^T = K · Q^T (t = 2m + kb), with exp2 / E4M3 / row sums of tile j:
-  // slot t handles values 2t, 2t+1 of the 32 (block t/8)
   float part0 = 0.0f, part1 = 0.0f, pair = 0.0f;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int m = t >> 1, kb = t & 1;
     sn[kb] = mfma_bf16(as_bf16x8(kv[t]), qop[m], m == 0 ? v16f{} : sn[kb]);
-    if (t + 8 < 16) kv[t + 8] = kread(kt, t + 8);
+    if (t + 4 < 16) kv[t + 4] = kread(kt, t + 4);
+    if (t >= 8) {
+      const int c = (t - 8) >> 1, h = (t - 8) & 1;
+      vv[t - 8] = *reinterpret_cast<const uint4*>(vt + c * 32 * kVPitch + 16 * h);
+    }
     {
-      const int blk = t >> 3, i = 2 * (t & 7);
-      const float bias = blk ? bias1 : bias0;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][i], c1, bias));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][i + 1], c1, bias));
-      const int w = 4 * blk + (i >> 2);
+      const int blk = t >> 3, i = 2 * (t & 7), w = 4 * blk + (i >> 2);
+      const float p0 = pv[blk][i], p1 = pv[blk][i + 1];
       if ((i & 2) == 0) {
-        pn[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pp[w], false);
+        pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], false);
         pair = p0 + p1;
       } else {
-        pn[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pn[w], true);
+        pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], true);
         const float q4 = pair + (p0 + p1);
         if (blk) part1 = (i == 2) ? q4 : part1 + q4;
         else part0 = (i == 2) ? q4 : part0 + q4;
@@ -272,31 +215,108 @@ __device__ __forceinline__ void step(int j, v16f (&sc)[2], v16f (&sn)[2], const 
     }
     KQ_FENCE();
   }
+  lsum += __builtin_amdgcn_ldexpf(part0, (int)d0p) + __builtin_amdgcn_ldexpf(part1, (int)d1p);
+  // keep the conversions in the slots above (the compiler would otherwise sink them past the
+  // masking branch, next to BMM2)
+  asm volatile("" ::"v"(pop), "v"(lsum));
+  {
+    const int k0 = G.kbase + j * kBN;
+    if (k0 + kBN > G.n) mask_tail(sn, k0, G);
+  }
+  KQ_FENCE();
+  uint2 ka, kb2, kc, kd;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    o[c] = mfma_f8_scaled(cat8(vv[2 * c], vv[2 * c + 1]), pop, o[c], pscale);
+    // block maxima: elements 4c .. 4c + 3 of each block
+    if (c == 0) {
+      mx0 = fmaxf(fmaxf(sn[0][0], sn[0][1]), fmaxf(sn[0][2], sn[0][3]));
+      mx1 = fmaxf(fmaxf(sn[1][0], sn[1][1]), fmaxf(sn[1][2], sn[1][3]));
+    } else {
+      mx0 = fmaxf(fmaxf(mx0, sn[0][4 * c]), fmaxf(sn[0][4 * c + 1], fmaxf(sn[0][4 * c + 2], sn[0][4 * c + 3])));
+      mx1 = fmaxf(fmaxf(mx1, sn[1][4 * c]), fmaxf(sn[1][4 * c + 1], fmaxf(sn[1][4 * c + 2], sn[1][4 * c + 3])));
+    }
+    if (c == 3) {
+      mx0 = max_with_partner(mx0);
+      mx1 = max_with_partner(mx1);
+    }
+    if (c == 0) {
+      ka = e4m3x4_to_bf16(kx.x);
+      kb2 = e4m3x4_to_bf16(kx.y);
+    } else if (c == 1) {
+      kc = e4m3x4_to_bf16(kx.z);
+      kd = e4m3x4_to_bf16(kx.w);
+    } else if (c == 2) {
+      uint8_t* kb = Ks + (cur ^ 1) * kKStage + G.kw;
+      *reinterpret_cast<uint4*>(kb) = make_uint4(ka.x, ka.y, kb2.x, kb2.y);
+      *reinterpret_cast<uint4*>(kb + 16) = make_uint4(kc.x, kc.y, kd.x, kd.y);
+      stage_v(Vs, cur, G, vx);
+    } else {
+      // past the end the loads return zeros and nothing reads the stages they fill
+      kx = bload16(G.krs, (uint32_t)(j + 2) * kBN * kD + G.ko);
+      vx = bload16(G.vrs, G.vo + (uint32_t)(j + 1) * kBN);
+    }
+    KQ_FENCE();
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
 
-  float d0 = fmaxf(mb0 - m_ref, -126.0f);       // weights below 2^-126 of the reference:
-  float d1 = fmaxf(mb1 - m_ref, -126.0f);       // negligible
-  m_top = fmaxf(m_top, fmaxf(mb0, mb1));
-  const float lsum_in = lsum;
-  lsum += __builtin_amdgcn_ldexpf(part0, (int)d0) + __builtin_amdgcn_ldexpf(part1, (int)d1);
-  // The codes and sums are consumed only by the next step; this empty use keeps them in the
-  // slots above instead of letting the compiler sink them past the branch and the barrier.
-  asm volatile("" ::"v"(pn), "v"(lsum));
+// VALU phase j of a wave: softmax of tile j on the scores s (in place: s becomes 448 p), from
+// the block maxima mx0, mx1 the matrix-core phase left.
+// BMM2's P operand is E4M3 with an E8M0 block scale per 32-key block: block kb holds the s[kb]
+// values of both lanes of a row (bytes 0-15 / 16-31 of each lane's operand), and lane group g
+// supplies the scale of block g.  Each block is quantized against its own integer offset
+// M_kb = ceil(max t over the block) (so p <= 1 and 448 p fits E4M3) and carries
+// 2^(M_kb - m_ref) as its scale: no accumulator rescale when the running maximum grows.
+// Codes differ from full-row ones by exact powers of two, which E4M3 rounding preserves in its
+// normal range.  Outputs the block offsets d0, d1 (relative to m_ref) and the scale byte.
+__device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float mx1,
+                                           float& m_ref, float& m_top, float& lsum,
+                                           v16f (&o)[4], int& pscale, float& d0o, float& d1o,
+                                           const Geo& G) {
+  const float c1 = G.c1;
+  float mb0 = ceilf(mx0 * c1), mb1 = ceilf(mx1 * c1);
+  if (j == 0) {                    // row reference: the row's offset on the first tile
+    const float mr = fmaxf(mb0, mb1);
+    m_ref = (mr == -INFINITY) ? 0.0f : mr;
+  }
+  if (mx0 == -INFINITY) mb0 = m_ref;             // whole block masked: p = 0 below
+  if (mx1 == -INFINITY) mb1 = m_ref;
+  float d0 = mb0 - m_ref, d1 = mb1 - m_ref;
   if (__builtin_expect(__any(fmaxf(d0, d1) > 64.0f), 0)) {
     // keep 2^d far from float32 overflow: move the row reference up, rescale exactly
     const float up = fmaxf(fmaxf(d0, d1) - 32.0f, 0.0f);
     const float alpha = __builtin_amdgcn_ldexpf(1.0f, -(int)up);
+    lsum *= alpha;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[c][i] *= alpha;
     m_ref += up;
-    d0 = fmaxf(d0 - up, -126.0f);
-    d1 = fmaxf(d1 - up, -126.0f);
-    lsum = lsum_in * alpha + __builtin_amdgcn_ldexpf(part0, (int)d0) +
-           __builtin_amdgcn_ldexpf(part1, (int)d1);
+    d0 -= up;
+    d1 -= up;
   }
+  d0 = fmaxf(d0, -126.0f);         // weights below 2^-126 of the reference: negligible
+  d1 = fmaxf(d1, -126.0f);
+  m_top = fmaxf(m_top, fmaxf(mb0, mb1));
   pscale = 127 + (int)(G.g ? d1 : d0);
-  __syncthreads();
+  d0o = d0;
+  d1o = d1;
+  const float bias0 = kLog2_448 - mb0, bias1 = kLog2_448 - mb1;
+  // in place and in groups of 8, so that each exp2 issues eight instructions after the fma it
+  // reads (a shared temporary would chain all 64 instructions on their latencies)
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int kb = h >> 1, i0 = 8 * (h & 1);
+    const float bias = kb ? bias1 : bias0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[kb][i0 + i] = __builtin_fmaf(s[kb][i0 + i], c1, bias);
+    KQ_FENCE();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[kb][i0 + i] = __builtin_amdgcn_exp2f(s[kb][i0 + i]);
+  }
+  // the values are consumed by the next matrix-core phase; keep them computed here
+  asm volatile("" ::"v"(s[0]), "v"(s[1]));
 }
 
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int nqb) {
@@ -361,7 +381,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     G.vread = r * kVPitch + 32 * g;
     G.n = N;
     G.g = g;
-    G.kbase = t_begin * kBN;
+    G.kbase = __builtin_amdgcn_readfirstlane(t_begin * kBN);
     G.c1 = a.c1;
   }
 
@@ -370,62 +390,47 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[c][i] = 0.0f;
-  v16f sA[2], sB[2];
-  v8i pA = {0, 0, 0, 0, 0, 0, 0, 0}, pB = pA;   // P codes; "tile -1" has none
-  int pscale = 127;
-  float m_ref = 0.0f;        // per-row reference offset (integer-valued), from tile 0
+  v16f sA[2], sB[2];                            // scores / 448 p of two consecutive tiles
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sB[0][i] = sB[1][i] = 0.0f;   // "tile -1": p = 0
+  v8i pop = {0, 0, 0, 0, 0, 0, 0, 0};
+  int pscale = 127;          // E8M0 scale of this lane group's P block (see valu_phase)
+  float d0 = 0.0f, d1 = 0.0f;  // block offsets of the last softmaxed tile, relative to m_ref
+  float m_ref = 0.0f;        // per-row reference offset (integer-valued), set on tile 0
   float m_top = -INFINITY;   // largest block offset seen (for the row statistics)
   float lsum = 0.0f;         // partial row sum of 448 p * 2^(M_kb - m_ref) over this lane's keys
-  const int ntiles = t_end - t_begin;            // tiles of this workgroup's key range
-  const int nfull = ntiles - 1;                  // steps before the (masked) last one
+  const int ntiles = __builtin_amdgcn_readfirstlane(t_end - t_begin);   // tiles of this range
+  const int grp = __builtin_amdgcn_readfirstlane(w >> 2);    // 0: waves 0-3, 1: waves 4-7 (one per SIMD each)
 
-  // Prologue: K(0) staged and multiplied (scores of tile 0 land in sA, or in sB when the
-  // number of full steps is odd, so that the paired loop below always starts from sA);
-  // K(1) staged, V^T(-1) = 0; kx/vx then hold K(2)/V^T(0).
-  uint4 kx = bload16(G.krs, G.ko), vx;
+  // Ping-pong schedule.  Every wave alternates a matrix-core phase (mfma_phase: BMM1 of tile j,
+  // the P codes and row sums of tile j-1, BMM2 of tile j-1, staging) and a VALU phase
+  // (valu_phase: softmax of tile j).  Group 1 runs half a period behind group 0, so on every
+  // SIMD one wave is in its matrix-core phase while the other is in its VALU phase; workgroup
+  // barriers separate the phases.  Phase 2j: group 0 MFMA(j), group 1 VALU(j-1); phase 2j+1:
+  // group 0 VALU(j), group 1 MFMA(j).  K(j) and V(j-1) are read in phases 2j and 2j+1; K(j+1)
+  // and V(j) are written to the other buffers in the same two phases (half by each group) and
+  // are complete before phase 2j+2.  Both groups pass 2 * ntiles + 4 barriers.
+  uint4 kx = bload16(G.krs, G.ko), vx;           // K(0): all 512 chunks
   stage_k(Ks, 0, G, kx);
-  *reinterpret_cast<uint4*>(Vs + kVStage + G.vw) = make_uint4(0, 0, 0, 0);
-  kx = bload16(G.krs, (uint32_t)kBN * kD + G.ko);
+  *reinterpret_cast<uint4*>(Vs + kVStage + G.vw) = make_uint4(0, 0, 0, 0);   // "V(-1)" = 0
+  kx = bload16(G.krs, (uint32_t)kBN * kD + G.ko);  // K(1): this thread's chunk
+  vx = bload16(G.vrs, G.vo);                       // V(0)
   __syncthreads();
-  if (nfull & 1) bmm1_plain(sB, Ks, 0, G, qop);
-  else bmm1_plain(sA, Ks, 0, G, qop);
-  stage_k(Ks, 1, G, kx);
-  kx = bload16(G.krs, (uint32_t)2 * kBN * kD + G.ko);
-  vx = bload16(G.vrs, G.vo);
-  {
-    // row reference m_ref = the row's offset on tile 0
-    v16f (&s0)[2] = (nfull & 1) ? sB : sA;
-    v16f t0[2] = {s0[0], s0[1]};
-    if (G.kbase + kBN > N) mask_tail(t0, G.kbase, G);
-    float mx = t0[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, t0[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, t0[1][i]);
-    mx = max_with_partner(mx);
-    m_ref = (mx == -INFINITY) ? 0.0f : ceilf(mx * G.c1);
+  if (grp == 1) __syncthreads();
+  float mx0, mx1;            // block maxima of the tile just multiplied
+  for (int j = 0;; j += 2) {
+    mfma_phase(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
+    __syncthreads();
+    if (j < ntiles) valu_phase(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, G);
+    __syncthreads();
+    if (j + 1 > ntiles) break;
+    mfma_phase(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
+    __syncthreads();
+    if (j + 1 < ntiles) valu_phase(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, G);
+    __syncthreads();
+    if (j + 2 > ntiles) break;
   }
-  __syncthreads();
-
-  int j = 0;
-  if (nfull & 1) {
-    step<false>(0, sB, sA, pB, pA, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
-    j = 1;
-  }
-  for (; j < nfull; j += 2) {
-    step<false>(j, sA, sB, pA, pB, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
-    step<false>(j + 1, sB, sA, pB, pA, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
-  }
-  step<true>(nfull, sA, sB, pA, pB, pscale, o, m_ref, m_top, lsum, kx, vx, qop, Ks, Vs, G);
-  {
-    // BMM2 of the last tile
-    const uint8_t* vt = Vs + (nfull & 1) * kVStage + G.vread;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      o[c] = mfma_f8_scaled(cat8(*reinterpret_cast<const uint4*>(vt + c * 32 * kVPitch),
-                                 *reinterpret_cast<const uint4*>(vt + c * 32 * kVPitch + 16)),
-                            pB, o[c], pscale);
-  }
+  if (grp == 0) __syncthreads();
 
   // ---- epilogue: O = acc * s_v / sum(448 p); lane (r, g) holds d = 32c + 8(i/4) + 4g + i%4
   const float ltot = lsum + __shfl_xor(lsum, 32);      // sum of 448 p relative to m_ref
