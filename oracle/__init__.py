@@ -24,4 +24,5 @@ Modules:
   rope       3-axis rotary position embedding (table and rotation)
   attention  R3 quantized attention (gated), R1 variant and FP64 reference (reported)
   pipeline   the whole path for one workload: RoPE -> FP4 -> calibrate -> FP8 -> attention
+  gemm       quantized projection GEMMs (per-tensor FP8 W8A8, per-block MXFP4), exact float64
 """

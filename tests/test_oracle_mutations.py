@@ -5,9 +5,11 @@ import pytest
 
 import test_oracle_attention as TA
 import test_oracle_formats as TF
+import test_oracle_gemm as TG
 import test_oracle_quant as TQ
 from oracle import attention as A
 from oracle import formats as F
+from oracle import gemm as G
 from oracle import quant as Qz
 from oracle import rope as R
 
@@ -58,7 +60,32 @@ def _apply_wrong_sign(x_f32, tab):
     return y
 
 
+def _gemm_fp8_no_weight_scale(a8, b8, s_a, s_b):
+    return (F.e4m3_decode(a8) @ F.e4m3_decode(b8).T) * float(s_a)     # planted: s_b dropped
+
+
+def _unpack_high_nibble_first(codes, scales, block=32):
+    codes = np.asarray(codes, dtype=np.uint8)
+    c = np.stack([codes >> 4, codes & 0xF], axis=-1).reshape(codes.shape[:-1] + (-1,))
+    return F.e2m1_decode(c) * F.e8m0_decode(np.repeat(np.asarray(scales), block, axis=-1))
+
+
+def _unpack_block_16(codes, scales, block=32):
+    codes = np.asarray(codes, dtype=np.uint8)
+    c = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (-1,))
+    s = np.repeat(np.asarray(scales), 16, axis=-1)                   # planted: 16-blocks
+    s = np.concatenate([s, s], axis=-1)[..., : c.shape[-1]]
+    return F.e2m1_decode(c) * F.e8m0_decode(s)
+
+
 MUTATIONS = {
+    "gemm fp8 weight scale dropped": (lambda mp: mp.setattr(G, "gemm_fp8", _gemm_fp8_no_weight_scale),
+                                      [TG.test_fp8_all_ones_closed_form,
+                                       TG.test_fp8_one_hot_rows_select_weight_columns]),
+    "fp4 unpack high nibble first": (lambda mp: mp.setattr(Qz, "fp4_unpack", _unpack_high_nibble_first),
+                                     [TG.test_mxfp4_one_hot_rows_select_weight_columns]),
+    "fp4 unpack 16-element blocks": (lambda mp: mp.setattr(Qz, "fp4_unpack", _unpack_block_16),
+                                     [TG.test_mxfp4_hand_computed_example]),
     "e4m3/e2m1 ties round down": (lambda mp: mp.setattr(F, "_nearest_code", _ties_down),
                                   [TF.test_e4m3_encode_midpoints_go_to_even_code,
                                    TF.test_e2m1_rounding_table]),
