@@ -161,6 +161,29 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
                                float* row_stats_or_null, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* Quantized projection GEMMs: C = A B^T for the linear layers around the attention, with
+ * per-tensor FP8 (W8A8) or per-block FP4 post-training quantization of both operands (blog
+ * section "Workflow and Quantization", the quantization config and its PTQ paragraph).
+ * A: activations [M][K], one row per token; B: weights [N][K], one row per output feature;
+ * both K-contiguous.  c_f32: device float32 [M][N], fully overwritten.  Products are taken on
+ * the matrix cores with float32 accumulation (summation order unspecified).
+ * Sizes: M, N, K >= 1; N % 4 == 0; (max(M, N) + 512) * (bytes per operand row) < 2^31;
+ * otherwise KQ_ERR_UNSUPPORTED (sizes < 1: KQ_ERR_INVALID_ARG). */
+
+/* FP8: a8 device uint8 [M][K], b8 device uint8 [N][K], E4M3 codes (kq_quantize_fp8_tensor with
+ * KQ_LAYOUT_ROWS writes them); s_a, s_b their per-tensor scales;
+ * C = s_a s_b sum_k E4M3(a8)_mk E4M3(b8)_nk.  K % 64 == 0. */
+kq_status kq_gemm_fp8(const uint8_t* a8, const uint8_t* b8, int64_t M, int64_t N, int64_t K,
+                      float s_a, float s_b, float* c_f32, hipStream_t stream);
+
+/* MXFP4: a_codes device uint8 [M][K/2], b_codes [N][K/2], E2M1 codes two per byte (even
+ * element in the low nibble); a_scales [M][K/32], b_scales [N][K/32] E8M0 bytes (4-byte
+ * aligned), one per 32 consecutive k (kq_quantize_fp4_block writes both);
+ * C = sum_k dq(a)_mk dq(b)_nk with dq = E2M1value * 2^(scale byte - 127).  K % 128 == 0. */
+kq_status kq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
+                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                        int64_t K, float* c_f32, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ import numpy as np
 __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSED",
            "kq_status_string", "kq_vt_ld", "kq_fp8_scales_from_amax", "kq_rope3_table",
            "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
-           "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws"]
+           "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws",
+           "kq_gemm_fp8", "kq_gemm_mxfp4"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_LAYOUT_ROWS = 0
@@ -55,6 +56,8 @@ _SIGNATURES = {
     "kq_attn_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], _I),
     "kq_attn_quant_fwd_ws": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P,
                               ctypes.c_size_t, _P], _I),
+    "kq_gemm_fp8": ([_P, _P, _I64, _I64, _I64, _F, _F, _P, _P], _I),
+    "kq_gemm_mxfp4": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
 }
 
 
@@ -239,3 +242,31 @@ def kq_attn_quant_fwd_ws(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_sca
         v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
         _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"), ws, nbytes,
         _stream(stream)), "kq_attn_quant_fwd_ws")
+
+
+def kq_gemm_fp8(a8, b8, s_a: float, s_b: float, c, stream=None):
+    """C = s_a s_b E4M3(a8) E4M3(b8)^T.  a8: uint8 [M, K]; b8: uint8 [N, K]; c: float32 [M, N]."""
+    import torch
+    M, K = a8.shape
+    N = b8.shape[0]
+    if b8.dim() != 2 or b8.shape[1] != K or tuple(c.shape) != (M, N):
+        raise KQError("expected a8 [M, K], b8 [N, K], c [M, N]")
+    _check(load().kq_gemm_fp8(
+        _dev(a8, torch.uint8, "a8"), _dev(b8, torch.uint8, "b8"), M, N, K, float(s_a),
+        float(s_b), _dev(c, torch.float32, "c"), _stream(stream)), "kq_gemm_fp8")
+
+
+def kq_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, stream=None):
+    """C = dq(a) dq(b)^T from packed E2M1 codes [rows, K/2] and E8M0 scales [rows, K/32];
+    c: float32 [M, N]."""
+    import torch
+    M, Kh = a_codes.shape
+    N = b_codes.shape[0]
+    K = 2 * Kh
+    if (b_codes.dim() != 2 or b_codes.shape[1] != Kh or a_scales.numel() != M * (K // 32)
+            or b_scales.numel() != N * (K // 32) or tuple(c.shape) != (M, N)):
+        raise KQError("expected codes [rows, K/2], scales [rows, K/32], c [M, N]")
+    _check(load().kq_gemm_mxfp4(
+        _dev(a_codes, torch.uint8, "a_codes"), _dev(a_scales, torch.uint8, "a_scales"),
+        _dev(b_codes, torch.uint8, "b_codes"), _dev(b_scales, torch.uint8, "b_scales"),
+        M, N, K, _dev(c, torch.float32, "c"), _stream(stream)), "kq_gemm_mxfp4")

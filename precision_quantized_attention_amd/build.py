@@ -14,7 +14,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkq.so")
 ARCH = "gfx950"
 
-SOURCES = ["kq_api.cpp", "quant.hip", "attn_fp8.hip"]
+SOURCES = ["kq_api.cpp", "quant.hip", "attn_fp8.hip", "gemm.hip"]
 
 # Packed FP32 VALU ops stay off: every FP32 instruction is a plain single-lane one.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

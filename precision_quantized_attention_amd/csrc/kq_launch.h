@@ -50,4 +50,17 @@ inline size_t attn_workspace_bytes(int rem, int split) {
 
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream);
 
+struct GemmParams {
+  const uint8_t* a;         // [M][K] E4M3 codes, or [M][K/2] packed E2M1 codes
+  const uint8_t* b;         // [N][K] / [N][K/2]
+  const uint8_t* a_scales;  // [M][K/32] E8M0 (FP4 only)
+  const uint8_t* b_scales;  // [N][K/32] E8M0 (FP4 only)
+  float* c;                 // [M][N]
+  int m, n, k;
+  float scale;              // s_a * s_b (FP8), 1 (FP4)
+};
+
+// C = A B^T; K % 64 == 0 (FP8) or K % 128 == 0 (FP4), N % 4 == 0.
+hipError_t launch_gemm(const GemmParams& p, bool fp4, hipStream_t stream);
+
 }  // namespace kq

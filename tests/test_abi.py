@@ -88,6 +88,23 @@ def test_validation_rejects_before_any_hip_call():
     assert S(0, 1, 128, 128, ctypes.byref(n)) == INVALID
     assert S(1, 1, 0, 128, ctypes.byref(n)) == INVALID
     assert S(1, 1, 128, 64, ctypes.byref(n)) == UNSUPPORTED
+    G8, G4 = lib.kq_gemm_fp8, lib.kq_gemm_mxfp4
+    assert G8(fake, fake, 256, 256, 256, 1.0, 1.0, None, None) == INVALID
+    assert G8(None, fake, 256, 256, 256, 1.0, 1.0, fake, None) == INVALID
+    assert G8(odd, fake, 256, 256, 256, 1.0, 1.0, fake, None) == INVALID
+    assert G8(fake, fake, 0, 256, 256, 1.0, 1.0, fake, None) == INVALID
+    assert G8(fake, fake, 256, 256, -64, 1.0, 1.0, fake, None) == INVALID
+    assert G8(fake, fake, 256, 256, 256, 0.0, 1.0, fake, None) == INVALID
+    assert G8(fake, fake, 256, 256, 256, 1.0, float("nan"), fake, None) == INVALID
+    assert G8(fake, fake, 256, 256, 256, 3e38, 3e38, fake, None) == INVALID    # s_a s_b = inf
+    assert G8(fake, fake, 256, 256, 96, 1.0, 1.0, fake, None) == UNSUPPORTED   # K % 64
+    assert G8(fake, fake, 256, 258, 256, 1.0, 1.0, fake, None) == UNSUPPORTED  # N % 4
+    assert G8(fake, fake, 1 << 20, 256, 4096, 1.0, 1.0, fake, None) == UNSUPPORTED  # > 2^31 B
+    assert G4(fake, fake, fake, fake, 256, 256, 256, None, None) == INVALID
+    assert G4(fake, None, fake, fake, 256, 256, 256, fake, None) == INVALID
+    assert G4(fake, fake, fake, ctypes.c_void_p(0x10002), 256, 256, 256, fake, None) == INVALID
+    assert G4(fake, fake, fake, fake, 256, 256, 192, fake, None) == UNSUPPORTED  # K % 128
+    assert G4(fake, fake, fake, fake, 256, 6, 256, fake, None) == UNSUPPORTED    # N % 4
 
 
 def test_scale_rule_matches_oracle():

@@ -13,6 +13,12 @@ the context; lpnh.cn "Flux.1 Kontext deep dive", sections 1 and 3: latents are
 cut into 2x2 patches and concatenated along the sequence, target tokens sit at
 positions (0, h, w) and context tokens at (i, h, w)).
 
+Projection GEMMs (the linear layers around the attention): activations [M, K] with one row
+per token (M = N of the sequence) and weights [N_out, K] with one row per output feature,
+K = H * d = 3072; the QKV projection has N_out = 3 * 3072, the output projection 3072.
+Activations ~ N(0, 1) with 1% outlier channels (x20) like Q, K, V, seed = seed; weights
+~ N(0, 1/K), seed = seed + 1; both rounded to bf16.
+
 Values: Q, K, V ~ N(0, 1) in float32 from numpy's PCG64 with
 seed = 1000 * config_index + t (t = 0, 1, 2 for Q, K, V), optionally with 1% of
 the H*d hidden channels (31 of 3072 at H=24, d=128; seed + 3 picks them) scaled
@@ -29,7 +35,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "CONFIGS", "config", "qkv_bits", "random_bits", "positions",
-           "bits_to_f32"]
+           "bits_to_f32", "GemmShape", "GEMM_SHAPES", "gemm_bits"]
 
 OUTLIER_FRACTION = 0.01
 OUTLIER_GAIN = 20.0
@@ -135,3 +141,37 @@ def positions(c: Workload) -> np.ndarray:
         pos[o:o + n, 2] = ww.reshape(-1)
         o += n
     return pos
+
+
+@dataclasses.dataclass(frozen=True)
+class GemmShape:
+    """One projection GEMM: C [M, N] = A [M, K] . W [N, K]^T."""
+    name: str
+    M: int
+    N: int
+    K: int
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+GEMM_SHAPES = [
+    GemmShape("kontext_1024_qkv_proj", 8704, 3 * 3072, 3072),
+    GemmShape("kontext_1024_out_proj", 8704, 3072, 3072),
+]
+
+
+def gemm_bits(M: int, N: int, K: int, seed: int, rows=None, cols=None):
+    """bf16 bits of (activations [M, K], weights [N, K]); `rows` / `cols` (index arrays or None)
+    select rows of each without changing their values."""
+    a = _draw((M, K), seed)
+    n_out = max(1, int(OUTLIER_FRACTION * K))
+    for c in np.random.Generator(np.random.PCG64(seed + 3)).choice(K, size=n_out, replace=False):
+        a[:, c] *= np.float32(OUTLIER_GAIN)
+    w = _draw((N, K), seed + 1) * np.float32(1.0 / np.sqrt(K))
+    if rows is not None:
+        a = a[np.asarray(rows)]
+    if cols is not None:
+        w = w[np.asarray(cols)]
+    return _to_bf16_bits(a), _to_bf16_bits(w)
