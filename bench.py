@@ -10,6 +10,12 @@ Prints ONE JSON line.  `value` = attention FLOPs (4*B*H*N^2*d) per step / step t
 TFLOP/s.  `roofline` describes the attention kernel alone, timed with HIP events on the
 stream it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload (a subset of query rows of a few heads).
+
+`--gemm fp8|mxfp4 --gemm-shape qkv|out` instead times one quantized projection GEMM around the
+attention (C = A W^T with A the 8704 token activations, K = 3072; N = 9216 for the QKV
+projection, 3072 for the output projection): codes and scales are prepared before the timed
+region, a step is one GEMM launch, and the line's cpu_baseline is the exact oracle GEMM on a
+bounded sample of activation rows.
 """
 from __future__ import annotations
 
@@ -24,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA peak
+FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 MFMA peak
 HBM_PEAK_GBS = 8000.0
 
 
@@ -36,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--gemm", choices=["fp8", "mxfp4"], default=None,
+                    help="time a projection GEMM instead of the attention step")
+    ap.add_argument("--gemm-shape", choices=["qkv", "out"], default="qkv")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="no timing: a plain copy of COPY_BYTES (counter calibration), then 3 "
                          "steps; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
@@ -116,11 +126,137 @@ def cpu_baseline(cfg, target_s):
                       f"({t_attn:.1f} s); quantization charged pro rata"}
 
 
+def gemm_main(args):
+    """One JSON line for a projection GEMM: a step is one kq_gemm_* launch on codes prepared
+    (quantized by the library's own kernels) before the timed region."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import precision_quantized_attention_amd as kq
+    from precision_quantized_attention_amd.pipeline import bf16_from_bits
+
+    shape = W.GEMM_SHAPES[0 if args.gemm_shape == "qkv" else 1]
+    M, N, K = shape.M, shape.N, shape.K
+    torch.cuda.set_device(0)
+    seed = 100 + N
+    a_bits, w_bits = W.gemm_bits(M, N, K, seed)
+    a, w = bf16_from_bits(a_bits), bf16_from_bits(w_bits)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    if args.gemm == "fp8":
+        ops = []
+        for x in (a, w):
+            am = torch.zeros(1, dtype=torch.float32, device="cuda")
+            kq.kq_amax_calibrate(x, am)
+            s_x, inv = kq.kq_fp8_scales_from_amax(float(am.item()))
+            y = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+            kq.kq_quantize_fp8_tensor(x, inv, y)
+            ops.append((y, s_x))
+        (a8, sa), (w8, sw) = ops
+        launch = lambda: kq.kq_gemm_fp8(a8, w8, sa, sw, c)
+        peak = FP8_PEAK_TFLOPS
+    else:
+        ops = []
+        for x in (a, w):
+            rows = x.shape[0]
+            codes = torch.empty((rows, K // 2), dtype=torch.uint8, device="cuda")
+            scales = torch.empty((rows, K // 32), dtype=torch.uint8, device="cuda")
+            kq.kq_quantize_fp4_block(x.view(-1, 128), codes.view(-1, 64), scales.view(-1, 4))
+            ops.append((codes, scales))
+        (ac, asc), (wc, wsc) = ops
+        launch = lambda: kq.kq_gemm_mxfp4(ac, asc, wc, wsc, c)
+        peak = FP4_PEAK_TFLOPS
+    stream = torch.cuda.current_stream()
+    if args.pmc_workload:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_workload": shape.name, "copy_bytes": COPY_BYTES, "steps": 3}))
+        return
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        launch()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    value = shape.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = shape.flops / (kern_ms * 1e-3) / 1e12
+    fmt_name = "FP8 E4M3 per-tensor (W8A8)" if args.gemm == "fp8" else "MXFP4 (E2M1, E8M0 per 32)"
+    out = {
+        "metric": f"quantized projection GEMM TFLOP/s ({fmt_name})",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if args.gemm == "fp8" else "mxfp4_e2m1", "data": "synthetic",
+        "config": {"workload": shape.name, "M": M, "N": N, "K": K,
+                   "step": "one GEMM launch on prepared codes, float32 C"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
+        "gemm_ms": round(kern_ms, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = gemm_cpu_baseline(args.gemm, shape, a_bits, w_bits,
+                                                args.cpu_seconds)
+    print(json.dumps(out))
+
+
+def gemm_cpu_baseline(fmt, shape, a_bits, w_bits, target_s):
+    """The oracle GEMM (exact float64) on successive 64-row blocks of the activations against
+    all weights, quantized by the oracle, until about `target_s` seconds."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from oracle import gemm as OG
+    from oracle import quant as Qz
+
+    t0 = time.perf_counter()
+    wf = W.bits_to_f32(w_bits)
+    if fmt == "fp8":
+        sw, iw = Qz.fp8_scales(Qz.amax(wf))
+        sa, ia = Qz.fp8_scales(Qz.amax(W.bits_to_f32(a_bits)))
+        wq = Qz.fp8_codes(wf, iw)
+    else:
+        wq = Qz.fp4_block_quant(wf)[:2]
+    t_w = time.perf_counter() - t0
+    rows, t = 0, 0.0
+    while t + t_w < target_s and rows < shape.M:
+        af = W.bits_to_f32(a_bits[rows:rows + 64])
+        t0 = time.perf_counter()
+        if fmt == "fp8":
+            OG.gemm_fp8(Qz.fp8_codes(af, ia), wq, sa, sw)
+        else:
+            ac, asc, _ = Qz.fp4_block_quant(af)
+            OG.gemm_mxfp4(ac, asc, *wq)
+        t += time.perf_counter() - t0
+        rows += len(af)
+    flops = 2.0 * rows * shape.N * shape.K
+    return {"value": flops / (t + t_w * rows / shape.M) / 1e12, "unit": "TFLOP/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{shape.name}: oracle quantization of the weights ({t_w:.1f} s, charged "
+                      f"pro rata) and the exact GEMM of {rows} activation rows ({t:.1f} s)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1"}))
         sys.exit(2)
+    if args.gemm:
+        gemm_main(args)
+        return
     import numpy as np
     import torch
     import workloads as W

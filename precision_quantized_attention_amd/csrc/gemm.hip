@@ -16,7 +16,8 @@
 // consecutive n.  A k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements)
 // through LDS: rows padded to 80 bytes (conflict-free 16-byte operand reads), three stages so
 // a step's tile is written two steps before it is multiplied and one barrier per step
-// suffices; the two waves of a SIMD hide each other's operand reads.
+// suffices; the HBM loads of a step are issued two steps before their LDS store (two register
+// sets), and the two waves of a SIMD hide each other's operand reads.
 //
 // Operand layouts of the f8f6f4 MFMA (measured): for E4M3, lane (r, g) holds row r with
 // k = 16g .. 16g+15 in bytes 0-15 and k = 32+16g .. in bytes 16-31; for E2M1, lane (r, g)
@@ -152,25 +153,25 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const uint32_t soff = (uint32_t)((sc_a ? mt : nt) * kTile + (tid & 255)) * sc_bytes;
   const int sloff = 2 * kOpStage + (sc_a ? 0 : kScStage) + 4 * (tid & 255);
 
-  uint4 xa0, xa1, xb0, xb1;
-  uint32_t xs = 0;
-#define KQ_LOAD(s)                                                        \
+  uint4 xa0[2], xa1[2], xb0[2], xb1[2];
+  uint32_t xs[2] = {0, 0};
+#define KQ_LOAD(s, R)                                                     \
   {                                                                       \
     const uint32_t o_ = (uint32_t)(s) * kRowBytes;                        \
-    xa0 = bload16(ar, goff_a + o_);                                       \
-    xa1 = bload16(ar, goff_a + row128 + o_);                              \
-    xb0 = bload16(br, goff_b + o_);                                       \
-    xb1 = bload16(br, goff_b + row128 + o_);                              \
-    if (kFP4) xs = bload4(scr, soff + 4 * (uint32_t)(s));                 \
+    xa0[R] = bload16(ar, goff_a + o_);                                    \
+    xa1[R] = bload16(ar, goff_a + row128 + o_);                           \
+    xb0[R] = bload16(br, goff_b + o_);                                    \
+    xb1[R] = bload16(br, goff_b + row128 + o_);                           \
+    if (kFP4) xs[R] = bload4(scr, soff + 4 * (uint32_t)(s));              \
   }
-#define KQ_STORE(stage)                                                   \
+#define KQ_STORE(stage, R)                                                \
   {                                                                       \
     uint8_t* st_ = lds + (stage) * kStage;                                \
-    *reinterpret_cast<uint4*>(st_ + loff) = xa0;                          \
-    *reinterpret_cast<uint4*>(st_ + loff + 128 * kPitch) = xa1;           \
-    *reinterpret_cast<uint4*>(st_ + kOpStage + loff) = xb0;               \
-    *reinterpret_cast<uint4*>(st_ + kOpStage + loff + 128 * kPitch) = xb1; \
-    if (kFP4) *reinterpret_cast<uint32_t*>(st_ + sloff) = xs;             \
+    *reinterpret_cast<uint4*>(st_ + loff) = xa0[R];                       \
+    *reinterpret_cast<uint4*>(st_ + loff + 128 * kPitch) = xa1[R];        \
+    *reinterpret_cast<uint4*>(st_ + kOpStage + loff) = xb0[R];            \
+    *reinterpret_cast<uint4*>(st_ + kOpStage + loff + 128 * kPitch) = xb1[R]; \
+    if (kFP4) *reinterpret_cast<uint32_t*>(st_ + sloff) = xs[R];          \
   }
 
   const int rbase_n = (wn * 128 + r) * kPitch + 16 * g;
@@ -185,25 +186,35 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[ni][mi][i] = 0.0f;
 
-  // Three stages: in step s the wave multiplies stage s % 3 (written in step s - 2), writes
-  // step s + 2's tile into stage (s + 2) % 3 (read last in step s - 1) and fetches step s + 3.
-  // Past the last step the fetches read bytes of the next rows (or zeros past the end) into
-  // stages nothing reads.
-  KQ_LOAD(0);
-  KQ_STORE(0);
-  KQ_LOAD(1);
-  KQ_STORE(1);
-  KQ_LOAD(2);
+  // Step s stores register set s % 2 (step s + 2, fetched in step s - 2) into stage (s + 2) % 3
+  // (read last in step s - 1), fetches step s + 4 into the same set and multiplies stage s % 3
+  // (stored in step s - 2).  Past the last step the fetches read bytes of the next rows (or
+  // zeros past the end) into stages nothing reads.
+  KQ_LOAD(0, 0);
+  KQ_STORE(0, 0);
+  KQ_LOAD(1, 1);
+  KQ_STORE(1, 1);
+  KQ_LOAD(2, 0);
+  KQ_LOAD(3, 1);
   __syncthreads();
   int st_mul = 0, st_wr = 2;
-  for (int s = 0; s < nsteps; ++s) {
-    KQ_STORE(st_wr);
-    KQ_LOAD(s + 3);
+  for (int s = 0; s < nsteps; s += 2) {
+    KQ_STORE(st_wr, 0);
+    KQ_LOAD(s + 4, 0);
     KQ_FENCE();
     kstep<kFP4>(acc, lds + st_mul * kStage, rbase_n, rbase_m, sbase_n, sbase_m, g);
     __syncthreads();
     st_mul = st_mul == 2 ? 0 : st_mul + 1;
     st_wr = st_wr == 2 ? 0 : st_wr + 1;
+    if (s + 1 < nsteps) {
+      KQ_STORE(st_wr, 1);
+      KQ_LOAD(s + 5, 1);
+      KQ_FENCE();
+      kstep<kFP4>(acc, lds + st_mul * kStage, rbase_n, rbase_m, sbase_n, sbase_m, g);
+      __syncthreads();
+      st_mul = st_mul == 2 ? 0 : st_mul + 1;
+      st_wr = st_wr == 2 ? 0 : st_wr + 1;
+    }
   }
 #undef KQ_LOAD
 #undef KQ_STORE
