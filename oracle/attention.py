@@ -25,6 +25,19 @@ below 2^53 units: a float64 matrix product returns the exact sum in any order.
 raw * c1 is formed in float64 and rounded once to float32 (in the rare case that
 the float64 product itself rounds, this is a double rounding of at most 1 ulp).
 
+R3 with a native MXFP4 BMM1 (a hardware-native variant, not the pages' numerics: the pages
+keep both products in FP8).  Q and K stay in their per-block FP4 form (E2M1 codes with an E8M0
+scale per 32 elements of d, the output of the FP4 fake-quantizer) and BMM1 multiplies the
+dequantized values directly, without the per-tensor FP8 step:
+
+  raw_ij = sum_k dq4(q)_ik dq4(k)_jk,  dq4 = E2M1 value * 2^(scale byte - 127)
+  t_ij   = fl32(raw_ij * c1),  c1 = fl32(sm_scale log2(e))
+
+and the rest as R3 (V, P in FP8).  raw is exact in float64: within one 32-block the products
+share the scale 2^(e_q + e_k) and are multiples of 1/4 of it below 36, so each block's sum
+is exact, and the four block sums of d = 128 are exact while their scales stay within
+2^(53 - 13) of each other (data-derived block exponents differ by far less).
+
 R1 (reported, not gated): the literal FakeQuantize on the normalized P = p/l with
 a per-tensor scale s_P = amax_P / 448 calibrated over the whole P tensor.
 FP64 reference (reported, not gated): softmax(Q K^T sm_scale) V on the
@@ -92,6 +105,34 @@ def attention_r3(q8, k8, v8, s_q, s_k, s_v, sm_scale, rows=None, chunk: int = 25
             for r0 in range(0, len(rows), chunk):
                 rr = rows[r0:r0 + chunk]
                 Qv = F.e4m3_decode(q8[b, h, rr])
+                O[b, h, r0:r0 + len(rr)], M[b, h, r0:r0 + len(rr)], L[b, h, r0:r0 + len(rr)] = \
+                    r3_rows(Qv, Kv, Vv, c1, c2)
+    return O, M, L
+
+
+def attention_r3_mxfp4(q_codes, q_scales, k_codes, k_scales, v8, s_v, sm_scale, rows=None,
+                       chunk: int = 256):
+    """R3 with BMM1 on the FP4 block-quantized Q and K (see the module docstring).
+
+    q_codes, k_codes: uint8 [B, H, N, d/2] packed E2M1 (even element in the low nibble);
+    q_scales, k_scales: uint8 [B, H, N, d/32] E8M0; v8: uint8 [B, H, N, d] E4M3 codes of V
+    (token-major) with per-tensor scale s_v.  Returns (O, M, l) like attention_r3.
+    """
+    from . import quant as Qz
+    B, H, N = q_codes.shape[:3]
+    d = 2 * q_codes.shape[3]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    c1, c2 = constants(1.0, 1.0, s_v, sm_scale)
+    O = np.empty((B, H, len(rows), d), np.float32)
+    M = np.empty((B, H, len(rows)), np.float64)
+    L = np.empty((B, H, len(rows)), np.float32)
+    for b in range(B):
+        for h in range(H):
+            Kv = Qz.fp4_unpack(k_codes[b, h], k_scales[b, h])
+            Vv = F.e4m3_decode(v8[b, h])
+            for r0 in range(0, len(rows), chunk):
+                rr = rows[r0:r0 + chunk]
+                Qv = Qz.fp4_unpack(q_codes[b, h, rr], q_scales[b, h, rr])
                 O[b, h, r0:r0 + len(rr)], M[b, h, r0:r0 + len(rr)], L[b, h, r0:r0 + len(rr)] = \
                     r3_rows(Qv, Kv, Vv, c1, c2)
     return O, M, L

@@ -224,3 +224,60 @@ def test_pipeline_fp4_rope_small():
         assert qz.amax[n] == float(np.max(np.abs(qz.fp4[n][2])))
     O, _, _ = P.attention(qz)
     assert np.all(np.isfinite(O))
+
+
+# ---------------------------------------------------------------- native MXFP4 BMM1 variant
+
+_E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # OCP MX E2M1, codes 0-7
+
+
+def _fp4_operands(shape, seed, lo=119, hi=133):
+    """Random E2M1 elements (all 16 codes) packed by hand (even element in the low nibble),
+    E8M0 scales in [lo, hi], and their values computed here from the OCP table: every value
+    E2M1 * 2^e with -8 <= e <= 6 is a multiple of 2^-9 below 448, i.e. exact in E4M3."""
+    B, H, N, d = shape
+    rng = np.random.default_rng(seed)
+    nib = rng.integers(0, 16, size=(B, H, N, d), dtype=np.uint8)
+    scales = rng.integers(lo, hi + 1, size=(B, H, N, d // 32), dtype=np.uint8)
+    sign = np.where(nib & 8, -1.0, 1.0)
+    values = sign * _E2M1_MAGS[nib & 7] * np.repeat(2.0 ** (scales.astype(np.float64) - 127),
+                                                     32, axis=-1)
+    codes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return codes, scales, values
+
+
+def _pin_r3_mxfp4_equals_fp8_r3():
+    shape = (1, 2, 96, 128)
+    qc, qs, qv = _fp4_operands(shape, 1)
+    kc, ks, kv = _fp4_operands(shape, 2)
+    v8 = _codes(shape, 3)
+    q8, k8 = F.e4m3_encode(qv), F.e4m3_encode(kv)
+    assert np.array_equal(F.e4m3_decode(q8), qv) and np.array_equal(F.e4m3_decode(k8), kv)
+    sv, sm = np.float32(0.02), np.float32(1 / math.sqrt(128))
+    o4, m4, l4 = A.attention_r3_mxfp4(qc, qs, kc, ks, v8, sv, sm)
+    o8, m8, l8 = A.attention_r3(q8, k8, v8, 1.0, 1.0, sv, sm)
+    assert np.array_equal(o4, o8) and np.array_equal(m4, m8) and np.array_equal(l4, l8)
+
+
+def test_r3_mxfp4_equals_fp8_r3_when_fp4_values_are_e4m3_exact():
+    """When every FP4 value is an exact E4M3 value, BMM1 on the FP4 operands and BMM1 on their
+    E4M3 codes with unit per-tensor scales are the same products: the MXFP4 variant must equal
+    the (independently pinned) FP8 R3 bit for bit."""
+    _pin_r3_mxfp4_equals_fp8_r3()
+
+
+def test_r3_mxfp4_rows_subset_and_real_quantizer_output():
+    """Sampled rows equal the full evaluation, and on the FP4 quantizer's own output the
+    result tracks unquantized float64 attention of the dequantized inputs."""
+    bits = [W.random_bits(1, 1, 200, 128, seed=90 + t, outliers=True) for t in range(3)]
+    x = [W.bits_to_f32(b) for b in bits]
+    (qc, qs, qd), (kc, ks, kd) = Qz.fp4_block_quant(x[0]), Qz.fp4_block_quant(x[1])
+    sv, iv = Qz.fp8_scales(Qz.amax(x[2]))
+    v8 = Qz.fp8_codes(x[2], iv)
+    sm = np.float32(1 / math.sqrt(128))
+    O, _, _ = A.attention_r3_mxfp4(qc, qs, kc, ks, v8, sv, sm)
+    rows = np.array([0, 7, 199])
+    Os, _, _ = A.attention_r3_mxfp4(qc, qs, kc, ks, v8, sv, sm, rows=rows)
+    assert np.array_equal(Os, O[:, :, rows])
+    ref = A.attention_fp64(qd, kd, F.e4m3_decode(v8) * float(sv), sm)
+    assert rel_l2(O, ref) < 3e-2

@@ -78,7 +78,19 @@ def _unpack_block_16(codes, scales, block=32):
     return F.e2m1_decode(c) * F.e8m0_decode(s)
 
 
+def _unpack_ignoring_scales(codes, scales, block=32):
+    codes = np.asarray(codes, dtype=np.uint8)
+    c = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (-1,))
+    return F.e2m1_decode(c)                                          # planted: no 2^e
+
+
 MUTATIONS = {
+    "mxfp4 attention with 16-element scale blocks": (
+        lambda mp: mp.setattr(Qz, "fp4_unpack", _unpack_block_16),
+        [TA._pin_r3_mxfp4_equals_fp8_r3]),
+    "mxfp4 attention ignores block scales": (
+        lambda mp: mp.setattr(Qz, "fp4_unpack", _unpack_ignoring_scales),
+        [TA._pin_r3_mxfp4_equals_fp8_r3]),
     "gemm fp8 weight scale dropped": (lambda mp: mp.setattr(G, "gemm_fp8", _gemm_fp8_no_weight_scale),
                                       [TG.test_fp8_all_ones_closed_form,
                                        TG.test_fp8_one_hot_rows_select_weight_columns]),
