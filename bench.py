@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--native-fp4", action="store_true",
+                    help="FP4 workloads: BMM1 on the FP4 Q, K (E2M1 + E8M0) instead of their "
+                         "FP8 re-quantization")
     ap.add_argument("--gemm", choices=["fp8", "mxfp4"], default=None,
                     help="time a projection GEMM instead of the attention step")
     ap.add_argument("--gemm-shape", choices=["qkv", "out"], default="qkv")
@@ -265,8 +268,11 @@ def main():
     c = W.config(args.config)
     torch.cuda.set_device(0)
     q, k, v = (bf16_from_bits(b) for b in W.qkv_bits(args.config))
+    if args.native_fp4 and c.mode != "fp4":
+        print(json.dumps({"error": "--native-fp4 needs an FP4 workload (--config 4 or 5)"}))
+        sys.exit(2)
     m = QuantizedSDPA(c.B, c.H, c.N, c.d, mode=c.mode,
-                      positions=W.positions(c) if c.rope else None)
+                      positions=W.positions(c) if c.rope else None, native_fp4=args.native_fp4)
     m.calibrate(q, k, v)                     # offline static calibration, not timed
     stream = torch.cuda.current_stream()
 
@@ -332,11 +338,15 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": c.name, "B": c.B, "H": c.H, "N": c.N, "d": c.d, "mode": c.mode,
-                   "step": "FP8 quantize Q,K,V + fused attention (static scales)"},
+                   "bmm1": "mxfp4" if args.native_fp4 else "fp8",
+                   "step": ("FP4 quantize Q,K,V (V then FP8) + attention with MXFP4 BMM1"
+                            if args.native_fp4 else
+                            "quantize Q,K,V to FP8 + fused attention (static scales)")},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": traffic_bytes()},
+                     "traffic": traffic_bytes() if args.config == 3 and not args.native_fp4
+                     else None},
         "pct_fp8_peak_step": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "attention_ms": round(attn_ms, 4),
         "quantize_ms": round(quant_ms, 4),

@@ -161,6 +161,23 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
                                float* row_stats_or_null, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* Attention with a native MXFP4 BMM1 (a hardware-native variant; the blog keeps both
+ * products in FP8, so this one is not its numerics): Q and K stay in the per-block FP4 form
+ * kq_quantize_fp4_block writes (E2M1 codes + an E8M0 scale per 32 elements of d, RoPE
+ * applied before quantization where used), and BMM1 multiplies their dequantized values on
+ * the matrix cores with float32 accumulation, without the per-tensor FP8 step:
+ *   raw = sum_d dq(q)_d dq(k)_d, dq = E2M1value * 2^(scale byte - 127);
+ *   t = raw * c1, c1 = sm_scale log2(e) (rounded once to float32);
+ * then softmax, P and BMM2 exactly as kq_attn_quant_fwd (V per-tensor FP8 with scale s_v).
+ * q_codes, k_codes: device uint8 [B*H][N][64]; q_scales, k_scales: device uint8 [B*H][N][4]
+ * (4-byte aligned); v8, v_layout, o_f32, row_stats_or_null as kq_attn_quant_fwd; workspace as
+ * kq_attn_quant_fwd_ws (NULL: no key split; size from kq_attn_workspace_size). */
+kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
+                            const uint8_t* k_codes, const uint8_t* k_scales, const uint8_t* v8,
+                            int v_layout, int B, int H, int N, int d, float s_v, float sm_scale,
+                            float* o_f32, float* row_stats_or_null, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 /* Quantized projection GEMMs: C = A B^T for the linear layers around the attention, with
  * per-tensor FP8 (W8A8) or per-block FP4 post-training quantization of both operands (blog
  * section "Workflow and Quantization", the quantization config and its PTQ paragraph).

@@ -21,7 +21,7 @@ __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSE
            "kq_status_string", "kq_vt_ld", "kq_fp8_scales_from_amax", "kq_rope3_table",
            "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
            "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws",
-           "kq_gemm_fp8", "kq_gemm_mxfp4"]
+           "kq_attn_mxfp4_fwd", "kq_gemm_fp8", "kq_gemm_mxfp4"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_LAYOUT_ROWS = 0
@@ -56,6 +56,8 @@ _SIGNATURES = {
     "kq_attn_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], _I),
     "kq_attn_quant_fwd_ws": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P,
                               ctypes.c_size_t, _P], _I),
+    "kq_attn_mxfp4_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P,
+                           ctypes.c_size_t, _P], _I),
     "kq_gemm_fp8": ([_P, _P, _I64, _I64, _I64, _F, _F, _P, _P], _I),
     "kq_gemm_mxfp4": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
 }
@@ -242,6 +244,33 @@ def kq_attn_quant_fwd_ws(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_sca
         v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
         _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"), ws, nbytes,
         _stream(stream)), "kq_attn_quant_fwd_ws")
+
+
+def kq_attn_mxfp4_fwd(q_codes, q_scales, k_codes, k_scales, v8t, s_v: float, sm_scale: float,
+                      o, workspace=None, row_stats=None, v_layout: int = KQ_LAYOUT_TRANSPOSED,
+                      stream=None):
+    """Attention with BMM1 on the FP4 block-quantized Q, K.  q_codes, k_codes: uint8
+    [B, H, N, 64]; q_scales, k_scales: uint8 [B, H, N, 4]; v8t, o, row_stats as
+    kq_attn_quant_fwd; workspace as kq_attn_quant_fwd_ws (or None)."""
+    import torch
+    B, H, N, dh = q_codes.shape
+    d = 2 * dh
+    if tuple(k_codes.shape) != (B, H, N, dh) or tuple(o.shape) != (B, H, N, d):
+        raise KQError("k_codes and o must match q_codes' shape")
+    if q_scales.numel() != B * H * N * (d // 32) or k_scales.numel() != B * H * N * (d // 32):
+        raise KQError("scales must be [B, H, N, d/32]")
+    if v_layout == KQ_LAYOUT_TRANSPOSED and v8t.numel() != B * H * d * kq_vt_ld(N):
+        raise KQError("v8t must be [B*H, d, kq_vt_ld(N)]")
+    if row_stats is not None and row_stats.numel() != B * H * N * 2:
+        raise KQError("row_stats must be [B, H, N, 2]")
+    ws = _opt(workspace, torch.uint8, "workspace")
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(load().kq_attn_mxfp4_fwd(
+        _dev(q_codes, torch.uint8, "q_codes"), _dev(q_scales, torch.uint8, "q_scales"),
+        _dev(k_codes, torch.uint8, "k_codes"), _dev(k_scales, torch.uint8, "k_scales"),
+        _dev(v8t, torch.uint8, "v8"), v_layout, B, H, N, d, float(s_v), float(sm_scale),
+        _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"), ws, nbytes,
+        _stream(stream)), "kq_attn_mxfp4_fwd")
 
 
 def kq_gemm_fp8(a8, b8, s_a: float, s_b: float, c, stream=None):

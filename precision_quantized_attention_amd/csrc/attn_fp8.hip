@@ -69,6 +69,10 @@ constexpr int kKPitch = kD * 2 + 16;        // bf16 K row in LDS + 16 bytes of p
 constexpr int kVPitch = kBN + 16;           // FP8 V^T row in LDS + 16 bytes of padding
 constexpr int kKStage = kBN * kKPitch;      // 17408 bytes
 constexpr int kVStage = kD * kVPitch;       // 10240 bytes
+// native MXFP4 BMM1: K rows stay packed E2M1 (64 bytes for d = 128) + an E8M0 scale dword
+constexpr int kK4Pitch = kD / 2 + 16;       // packed K row in LDS + 16 bytes of padding
+constexpr int kK4Codes = kBN * kK4Pitch;    // 5120 bytes
+constexpr int kK4Stage = kK4Codes + kBN * 4;  // + the 4 scale bytes of every key: 5376 bytes
 constexpr float kLog2_448 = 8.807354922057604f;
 
 #define KQ_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -105,6 +109,15 @@ __device__ __forceinline__ v16f mfma_f8_scaled(v8i a, v8i b, v16f c, int scale_b
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
 }
 
+// E2M1 x E2M1 (format codes 4, 4) with an E8M0 scale per 32-k block on both operands: lane
+// (r, g) holds k = 32g .. 32g + 31 of its row as 32 nibbles (low nibble first) in the low 16
+// bytes of its operand and supplies the scale byte of that block.
+__device__ __forceinline__ v16f mfma_fp4(uint4 a, uint4 b, v16f c, int scale_a, int scale_b) {
+  const v8i az = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bz = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(az, bz, c, 4, 4, 0, scale_a, 0, scale_b);
+}
+
 __device__ __forceinline__ v8i cat8(uint4 lo, uint4 hi) {
   v8i r;
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
@@ -130,16 +143,50 @@ __device__ __forceinline__ int krow_of_key(int kappa) {
 // Per-thread constants of a workgroup.
 struct Geo {
   __amdgpu_buffer_rsrc_t krs, vrs;   // K rows [N][128], V^T rows [128][ldv] of this (b, h)
+  __amdgpu_buffer_rsrc_t ksr;        // MXFP4: K scale dwords [N][4]
   uint32_t ko, vo;                   // this thread's staging chunk in the first tile
   int kw, vw;                        // its LDS destination within a stage
   int kread, vread;                  // this lane's operand read bases within a stage
+  int krole;                         // MXFP4 K staging: 0 codes, 1 scale dword, 2 none
+  int n4r;                           // MXFP4: this lane's scale dword index (row r) in a stage
   int n, g;
   int kbase;                         // first key of the workgroup's key range
   float c1;
 };
 
+// BMM1's Q operand, held in registers for the whole key loop.
+template <bool kFP4> struct QOp;
+template <> struct QOp<false> {
+  v8bf v[8];                         // bf16 values of the E4M3 codes, d = 16m + 8g .. +7
+};
+template <> struct QOp<true> {
+  uint4 c[2];                        // packed E2M1, d = 64h + 32g .. +31
+  int s[2];                          // E8M0 byte of block 2h + g
+};
+
+// This thread's part of K(tile) (tile counted from the key range's first tile); loads past
+// the end of the buffers return zeros.
+template <bool kFP4>
+__device__ __forceinline__ uint4 kload(const Geo& G, int tile) {
+  if constexpr (kFP4) {
+    if (G.krole == 0) return bload16(G.krs, (uint32_t)tile * kBN * (kD / 2) + G.ko);
+    if (G.krole == 1)
+      return make_uint4(__builtin_amdgcn_raw_buffer_load_b32(G.ksr, (uint32_t)tile * kBN * 4 + G.ko, 0, 0), 0u, 0u, 0u);
+    return make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    return bload16(G.krs, (uint32_t)tile * kBN * kD + G.ko);
+  }
+}
+
 // Stage K(tile) (FP8 codes in kx, converted to bf16) and V^T(tile) (vx) into buffer `buf`.
+template <bool kFP4>
 __device__ __forceinline__ void stage_k(uint8_t* Ks, int buf, const Geo& G, uint4 kx) {
+  if constexpr (kFP4) {
+    uint8_t* kb = Ks + buf * kK4Stage + G.kw;
+    if (G.krole == 0) *reinterpret_cast<uint4*>(kb) = kx;
+    else if (G.krole == 1) *reinterpret_cast<uint32_t*>(kb) = kx.x;
+    return;
+  }
   uint8_t* kb = Ks + buf * kKStage + G.kw;
   const uint2 a = e4m3x4_to_bf16(kx.x), b = e4m3x4_to_bf16(kx.y);
   const uint2 c = e4m3x4_to_bf16(kx.z), d = e4m3x4_to_bf16(kx.w);
@@ -177,25 +224,51 @@ __device__ __forceinline__ void mask_tail(v16f (&s)[2], int k0, const Geo& G) {
 // The wave runs this phase at raised priority: its few VALU instructions and the MFMA issues
 // behind them then win the arbitration against the other wave of the SIMD, which is in its
 // VALU phase, and the matrix pipe stays fed.
+// With kFP4 (native MXFP4 BMM1), the 4 MFMAs of BMM1 take the packed E2M1 K rows and their
+// E8M0 scales from LDS and the packed Q operand from registers; they issue in slots 0, 4, 8
+// and 12 of the same 16-slot loop (the P codes of tile j-1 fill every slot).
+template <bool kFP4>
 __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv)[2], v8i& pop,
                                            int pscale, float d0p, float d1p, v16f (&o)[4],
                                            float& lsum, uint4& kx, uint4& vx, float& mx0,
-                                           float& mx1, const v8bf (&qop)[8], uint8_t* Ks,
+                                           float& mx1, const QOp<kFP4>& qop, uint8_t* Ks,
                                            uint8_t* Vs, const Geo& G) {
   __builtin_amdgcn_s_setprio(1);
   const int cur = j & 1;
-  const uint8_t* kt = Ks + cur * kKStage + G.kread;
   const uint8_t* vt = Vs + (cur ^ 1) * kVStage + G.vread;
   uint4 kv[16], vv[8];
+  int ksa[4];
+  if constexpr (kFP4) {
+    // operand idx = 2h + kb: key block kb (LDS rows 32kb + r), d = 64h + 32g ..
+    const uint8_t* kt = Ks + cur * kK4Stage + G.kread;
+    const uint32_t* ksc = reinterpret_cast<const uint32_t*>(Ks + cur * kK4Stage + kK4Codes) + G.n4r;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) kv[t] = kread(kt, t);
+    for (int idx = 0; idx < 4; ++idx)
+      kv[idx] = *reinterpret_cast<const uint4*>(kt + (idx & 1) * 32 * kK4Pitch + 32 * (idx >> 1));
+    const uint32_t s0 = ksc[0], s1 = ksc[32];
+#pragma unroll
+    for (int idx = 0; idx < 4; ++idx)
+      ksa[idx] = (int)(((idx & 1) ? s1 : s0) >> (8 * (2 * (idx >> 1) + G.g))) & 0xFF;
+  } else {
+    const uint8_t* kt = Ks + cur * kKStage + G.kread;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kv[t] = kread(kt, t);
+  }
   KQ_FENCE();
   float part0 = 0.0f, part1 = 0.0f, pair = 0.0f;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
-    const int m = t >> 1, kb = t & 1;
-    sn[kb] = mfma_bf16(as_bf16x8(kv[t]), qop[m], m == 0 ? v16f{} : sn[kb]);
-    if (t + 4 < 16) kv[t + 4] = kread(kt, t + 4);
+    if constexpr (kFP4) {
+      if ((t & 3) == 0) {
+        const int idx = t >> 2, kb = idx & 1, h = idx >> 1;
+        sn[kb] = mfma_fp4(kv[idx], qop.c[h], h == 0 ? v16f{} : sn[kb], ksa[idx], qop.s[h]);
+      }
+    } else {
+      const int m = t >> 1, kb = t & 1;
+      sn[kb] = mfma_bf16(as_bf16x8(kv[t]), qop.v[m], m == 0 ? v16f{} : sn[kb]);
+      const uint8_t* kt = Ks + cur * kKStage + G.kread;
+      if (t + 4 < 16) kv[t + 4] = kread(kt, t + 4);
+    }
     if (t >= 8) {
       const int c = (t - 8) >> 1, h = (t - 8) & 1;
       vv[t - 8] = *reinterpret_cast<const uint4*>(vt + c * 32 * kVPitch + 16 * h);
@@ -240,20 +313,28 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
       mx0 = max_with_partner(mx0);
       mx1 = max_with_partner(mx1);
     }
-    if (c == 0) {
-      ka = e4m3x4_to_bf16(kx.x);
-      kb2 = e4m3x4_to_bf16(kx.y);
-    } else if (c == 1) {
-      kc = e4m3x4_to_bf16(kx.z);
-      kd = e4m3x4_to_bf16(kx.w);
-    } else if (c == 2) {
-      uint8_t* kb = Ks + (cur ^ 1) * kKStage + G.kw;
-      *reinterpret_cast<uint4*>(kb) = make_uint4(ka.x, ka.y, kb2.x, kb2.y);
-      *reinterpret_cast<uint4*>(kb + 16) = make_uint4(kc.x, kc.y, kd.x, kd.y);
-      stage_v(Vs, cur, G, vx);
+    if constexpr (kFP4) {
+      if (c == 2) {
+        stage_k<true>(Ks, cur ^ 1, G, kx);
+        stage_v(Vs, cur, G, vx);
+      }
     } else {
+      if (c == 0) {
+        ka = e4m3x4_to_bf16(kx.x);
+        kb2 = e4m3x4_to_bf16(kx.y);
+      } else if (c == 1) {
+        kc = e4m3x4_to_bf16(kx.z);
+        kd = e4m3x4_to_bf16(kx.w);
+      } else if (c == 2) {
+        uint8_t* kb = Ks + (cur ^ 1) * kKStage + G.kw;
+        *reinterpret_cast<uint4*>(kb) = make_uint4(ka.x, ka.y, kb2.x, kb2.y);
+        *reinterpret_cast<uint4*>(kb + 16) = make_uint4(kc.x, kc.y, kd.x, kd.y);
+        stage_v(Vs, cur, G, vx);
+      }
+    }
+    if (c == 3) {
       // past the end the loads return zeros and nothing reads the stages they fill
-      kx = bload16(G.krs, (uint32_t)(j + 2) * kBN * kD + G.ko);
+      kx = kload<kFP4>(G, j + 2);
       vx = bload16(G.vrs, G.vo + (uint32_t)(j + 1) * kBN);
     }
     KQ_FENCE();
@@ -319,8 +400,10 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
   asm volatile("" ::"v"(s[0]), "v"(s[1]));
 }
 
+template <bool kFP4>
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int nqb) {
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * kKStage];   // bf16 K tiles
+  // bf16 K tiles, or packed E2M1 K tiles + scales (kFP4)
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * (kFP4 ? kK4Stage : kKStage)];
   __shared__ __attribute__((aligned(16))) uint8_t Vs[2 * kVStage];   // FP8 V^T tiles
 
   // Work assignment.  Dispatch slots below a.nfull are whole query blocks, in an XCD-aware
@@ -353,31 +436,62 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
 
   // Q operand (bf16 values of the E4M3 codes): step m covers d = 16m .. 16m + 15; lane (r, g)
   // supplies query q, d = 16m + 8g .. +7.  Rows past N read as zeros.
-  v8bf qop[8];
-  {
+  // MXFP4: lane (r, g) holds query q's packed d = 64h + 32g .. +31 and the scale of that block.
+  QOp<kFP4> qop;
+  if constexpr (kFP4) {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + (int64_t)bh * N * (kD / 2), (uint32_t)N * (kD / 2));
+    const __amdgpu_buffer_rsrc_t qsr = make_rsrc(a.q_scales + (int64_t)bh * N * 4, (uint32_t)N * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qop.c[h] = bload16(qr, (uint32_t)q * (kD / 2) + 32 * h + 16 * g);
+    const uint32_t sd = __builtin_amdgcn_raw_buffer_load_b32(qsr, (uint32_t)q * 4, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qop.s[h] = (int)(sd >> (8 * (2 * h + g))) & 0xFF;
+  } else {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + (int64_t)bh * N * kD, (uint32_t)N * kD);
     const uint32_t qo = (uint32_t)q * kD + 8 * g;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const uint2 c = bload8(qr, qo + 16 * m);
       const uint2 lo = e4m3x4_to_bf16(c.x), hi = e4m3x4_to_bf16(c.y);
-      qop[m] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      qop.v[m] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
   }
 
   // Tile staging: a K tile is 512 FP8 chunks of 16 bytes (64 keys x 8) and a V^T tile 512
   // chunks (128 d-rows x 4); each thread owns chunk `tid` of both.
+  // MXFP4: a K tile is 256 chunks of 16 bytes (64 keys x 4), staged by waves 0-3, plus 64
+  // scale dwords, staged by wave 4.
   Geo G;
   {
-    const int kr = tid >> 3, kc = tid & 7;                 // key row, 16-byte column
     const int vd = tid >> 2, vc = tid & 3;                 // d row, 16-byte column
-    G.kw = krow_of_key(kr) * kKPitch + 32 * kc;
+    if constexpr (kFP4) {
+      const int kr = (tid >> 2) & 63, kc = tid & 3;        // key row, 16-byte column (waves 0-3)
+      G.krole = __builtin_amdgcn_readfirstlane(tid < 256 ? 0 : (tid < 320 ? 1 : 2));
+      G.krs = make_rsrc(a.k + (int64_t)bh * N * (kD / 2), (uint32_t)N * (kD / 2));
+      G.ksr = make_rsrc(a.k_scales + (int64_t)bh * N * 4, (uint32_t)N * 4);
+      if (G.krole == 1) {
+        const int ks = tid - 256;                          // key of this scale dword
+        G.kw = kK4Codes + krow_of_key(ks) * 4;
+        G.ko = (uint32_t)t_begin * kBN * 4 + ks * 4;
+      } else {
+        G.kw = krow_of_key(kr) * kK4Pitch + 16 * kc;
+        G.ko = (uint32_t)t_begin * kBN * (kD / 2) + kr * (kD / 2) + kc * 16;
+      }
+      G.kread = r * kK4Pitch + 16 * g;
+      G.n4r = r;
+    } else {
+      const int kr = tid >> 3, kc = tid & 7;               // key row, 16-byte column
+      G.krole = 0;
+      G.kw = krow_of_key(kr) * kKPitch + 32 * kc;
+      G.krs = make_rsrc(a.k + (int64_t)bh * N * kD, (uint32_t)N * kD);
+      G.ksr = G.krs;
+      G.ko = (uint32_t)t_begin * kBN * kD + kr * kD + kc * 16;
+      G.kread = r * kKPitch + 16 * g;
+      G.n4r = 0;
+    }
     G.vw = vd * kVPitch + 16 * vc;
-    G.krs = make_rsrc(a.k + (int64_t)bh * N * kD, (uint32_t)N * kD);
     G.vrs = make_rsrc(a.vt + (int64_t)bh * kD * a.ldv, (uint32_t)(kD * a.ldv));
-    G.ko = (uint32_t)t_begin * kBN * kD + kr * kD + kc * 16;
     G.vo = (uint32_t)(vd * a.ldv + vc * 16 + t_begin * kBN);
-    G.kread = r * kKPitch + 16 * g;
     G.vread = r * kVPitch + 32 * g;
     G.n = N;
     G.g = g;
@@ -410,21 +524,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   // group 0 VALU(j), group 1 MFMA(j).  K(j) and V(j-1) are read in phases 2j and 2j+1; K(j+1)
   // and V(j) are written to the other buffers in the same two phases (half by each group) and
   // are complete before phase 2j+2.  Both groups pass 2 * ntiles + 4 barriers.
-  uint4 kx = bload16(G.krs, G.ko), vx;           // K(0): all 512 chunks
-  stage_k(Ks, 0, G, kx);
+  uint4 kx = kload<kFP4>(G, 0), vx;              // K(0)
+  stage_k<kFP4>(Ks, 0, G, kx);
   *reinterpret_cast<uint4*>(Vs + kVStage + G.vw) = make_uint4(0, 0, 0, 0);   // "V(-1)" = 0
-  kx = bload16(G.krs, (uint32_t)kBN * kD + G.ko);  // K(1): this thread's chunk
+  kx = kload<kFP4>(G, 1);                          // K(1): this thread's chunk
   vx = bload16(G.vrs, G.vo);                       // V(0)
   __syncthreads();
   if (grp == 1) __syncthreads();
   float mx0, mx1;            // block maxima of the tile just multiplied
   for (int j = 0;; j += 2) {
-    mfma_phase(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
+    mfma_phase<kFP4>(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
     if (j < ntiles) valu_phase(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, G);
     __syncthreads();
     if (j + 1 > ntiles) break;
-    mfma_phase(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
+    mfma_phase<kFP4>(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
     if (j + 1 < ntiles) valu_phase(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, G);
     __syncthreads();
@@ -517,7 +631,10 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream) {
   const int nqb = (p.n + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)p.nfull + (int64_t)p.rem * p.split;
-  hipLaunchKernelGGL(attn_fp8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+  if (p.q_scales != nullptr)
+    hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+  else
+    hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split == 0) return e;
   const int64_t cblocks = ((int64_t)p.rem * kBM * 32 + 255) / 256;

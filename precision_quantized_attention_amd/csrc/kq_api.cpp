@@ -77,6 +77,7 @@ kq_status attn_params(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, i
   if (!isfinite(c1) || !isfinite((float)c1) || (float)c1 <= 0.0f) return KQ_ERR_INVALID_ARG;
   p->q = q8;
   p->k = k8;
+  p->q_scales = p->k_scales = nullptr;
   p->vt = v8;
   p->o = o_f32;
   p->stats = row_stats_or_null;
@@ -95,6 +96,21 @@ kq_status attn_params(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, i
 SplitPlan attn_plan(int B, int H, int N) {
   const int64_t nqb = ((int64_t)N + kq::kAttnRowsPerBlock - 1) / kq::kAttnRowsPerBlock;
   return plan_split((int64_t)B * H * nqb, (N + 63) / 64, device_cus());
+}
+
+// Key split of the last round through a caller workspace (NULL: none).
+kq_status attn_workspace(int B, int H, int N, void* workspace, size_t workspace_bytes,
+                         kq::AttnParams* p) {
+  if (workspace == nullptr) return KQ_OK;
+  if (!aligned(workspace, 16)) return KQ_ERR_INVALID_ARG;
+  const SplitPlan pl = attn_plan(B, H, N);
+  if (pl.split == 0) return KQ_OK;
+  if (workspace_bytes < kq::attn_workspace_bytes(pl.rem, pl.split)) return KQ_ERR_INVALID_ARG;
+  p->nfull = pl.nfull;
+  p->rem = pl.rem;
+  p->split = pl.split;
+  p->ws = static_cast<float*>(workspace);
+  return KQ_OK;
 }
 
 // Shared validation of the projection GEMMs: sizes, the K granule of one k-step, N a multiple
@@ -253,17 +269,8 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
   const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
                                    o_f32, row_stats_or_null, &p);
   if (st != KQ_OK) return st;
-  if (workspace != nullptr && !aligned(workspace, 16)) return KQ_ERR_INVALID_ARG;
-  if (workspace != nullptr) {
-    const SplitPlan pl = attn_plan(B, H, N);
-    if (pl.split > 0) {
-      if (workspace_bytes < kq::attn_workspace_bytes(pl.rem, pl.split)) return KQ_ERR_INVALID_ARG;
-      p.nfull = pl.nfull;
-      p.rem = pl.rem;
-      p.split = pl.split;
-      p.ws = static_cast<float*>(workspace);
-    }
-  }
+  const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
+  if (sw != KQ_OK) return sw;
   return from_hip(kq::launch_attn_fp8(p, stream));
 }
 
@@ -288,6 +295,24 @@ kq_status kq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
   p.a_scales = a_scales;
   p.b_scales = b_scales;
   return from_hip(kq::launch_gemm(p, true, stream));
+}
+
+kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
+                            const uint8_t* k_codes, const uint8_t* k_scales, const uint8_t* v8,
+                            int v_layout, int B, int H, int N, int d, float s_v, float sm_scale,
+                            float* o_f32, float* row_stats_or_null, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  kq::AttnParams p;
+  const kq_status st = attn_params(q_codes, k_codes, v8, v_layout, B, H, N, d, 1.0f, 1.0f, s_v,
+                                   sm_scale, o_f32, row_stats_or_null, &p);
+  if (st != KQ_OK) return st;
+  if (q_scales == nullptr || k_scales == nullptr) return KQ_ERR_INVALID_ARG;
+  if (!aligned(q_scales, 4) || !aligned(k_scales, 4)) return KQ_ERR_INVALID_ARG;
+  p.q_scales = q_scales;
+  p.k_scales = k_scales;
+  const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
+  if (sw != KQ_OK) return sw;
+  return from_hip(kq::launch_attn_fp8(p, stream));
 }
 
 }  // extern "C"

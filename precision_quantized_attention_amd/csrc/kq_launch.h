@@ -21,15 +21,17 @@ hipError_t launch_fp4_block(const uint16_t* x, int64_t rows, int d, uint8_t* cod
                             const float* rope_table, int64_t rope_tokens, hipStream_t stream);
 
 struct AttnParams {
-  const uint8_t* q;       // [BH][N][128] E4M3
-  const uint8_t* k;       // [BH][N][128] E4M3
+  const uint8_t* q;       // [BH][N][128] E4M3, or [BH][N][64] packed E2M1 (q_scales set)
+  const uint8_t* k;       // [BH][N][128] E4M3, or [BH][N][64] packed E2M1
+  const uint8_t* q_scales;  // MXFP4 BMM1: [BH][N][4] E8M0; nullptr: FP8 BMM1
+  const uint8_t* k_scales;  // MXFP4 BMM1: [BH][N][4] E8M0
   const uint8_t* vt;      // [BH][128][ldv] E4M3, zero beyond N
   float* o;               // [BH][N][128]
   float* stats;           // [BH][N][2] or nullptr
   int bh;
   int n;
   int64_t ldv;
-  float c1;               // s_q * s_k * sm_scale * log2(e), rounded once to float32
+  float c1;               // s_q * s_k * sm_scale * log2(e) (MXFP4: sm_scale * log2(e)), rounded once
   float s_v;
   // Key split of the last, partial round of query blocks (split == 0: none).  Query blocks
   // [0, nfull) run whole; each of the `rem` blocks after them runs as `split` workgroups over

@@ -22,7 +22,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (KQ_LAYOUT_TRANSPOSED, kq_amax_calibrate, kq_attn_quant_fwd_ws,
+from . import (KQ_LAYOUT_TRANSPOSED, kq_amax_calibrate, kq_attn_mxfp4_fwd, kq_attn_quant_fwd_ws,
                kq_attn_workspace_size,
                kq_fp8_scales_from_amax, kq_quantize_fp4_block, kq_quantize_fp8_tensor,
                kq_rope3_table, kq_vt_ld)
@@ -45,12 +45,17 @@ class QuantizedSDPA:
     mode "fp8": per-tensor FP8 Q/K/V.  mode "fp4": per-block FP4 Q/K/V, then per-tensor FP8.
     positions: optional int32 [N, 3] token positions; enables the 3-axis rotary embedding of
     Q and K before FP4 quantization (FP4 mode only).
+    native_fp4 (FP4 mode only): BMM1 multiplies the FP4 Q, K directly (E2M1 + E8M0 on the
+    matrix cores) instead of their per-tensor FP8 re-quantization; V still goes FP4 -> FP8.
     """
 
     def __init__(self, B, H, N, d=128, mode="fp8", positions=None, device="cuda",
-                 sm_scale=None, want_stats=False):
+                 sm_scale=None, want_stats=False, native_fp4=False):
         if mode not in ("fp8", "fp4"):
             raise ValueError(mode)
+        if native_fp4 and mode != "fp4":
+            raise ValueError("native_fp4 needs mode 'fp4'")
+        self.native_fp4 = native_fp4
         if positions is not None and mode != "fp4":
             raise ValueError("the rotary embedding is fused into the FP4 quantizer")
         self.B, self.H, self.N, self.d, self.mode = B, H, N, d, mode
@@ -105,6 +110,13 @@ class QuantizedSDPA:
             kq_quantize_fp8_tensor(q, self.scales["q"][1], b.q8)
             kq_quantize_fp8_tensor(k, self.scales["k"][1], b.k8)
             kq_quantize_fp8_tensor(v, self.scales["v"][1], b.v8t, layout=KQ_LAYOUT_TRANSPOSED)
+        elif self.native_fp4:
+            for n, x in (("q", q), ("k", k)):
+                codes, scales = b.fp4[n]
+                kq_quantize_fp4_block(x, codes, scales, rope=self._rope_for(n))
+            codes, scales = b.fp4["v"]
+            kq_quantize_fp4_block(v, codes, scales, dq=b.v_dq)
+            kq_quantize_fp8_tensor(b.v_dq, self.scales["v"][1], b.v8t, layout=KQ_LAYOUT_TRANSPOSED)
         else:
             for n, x, out in (("q", q, b.q8), ("k", k, b.k8)):
                 codes, scales = b.fp4[n]
@@ -120,10 +132,14 @@ class QuantizedSDPA:
             nbytes = kq_attn_workspace_size(self.B, self.H, self.N, self.d)
             self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=self.device)
                               if nbytes else False)
-        kq_attn_quant_fwd_ws(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
-                             self.scales["v"][0], self.sm_scale, b.o,
-                             self.workspace if self.workspace is not False else None,
-                             row_stats=b.stats)
+        ws = self.workspace if self.workspace is not False else None
+        if self.native_fp4:
+            (qc, qs), (kc, ks) = b.fp4["q"], b.fp4["k"]
+            kq_attn_mxfp4_fwd(qc, qs, kc, ks, b.v8t, self.scales["v"][0], self.sm_scale, b.o,
+                              ws, row_stats=b.stats)
+        else:
+            kq_attn_quant_fwd_ws(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
+                                 self.scales["v"][0], self.sm_scale, b.o, ws, row_stats=b.stats)
         return b.o
 
     def forward(self, q, k, v):

@@ -88,6 +88,19 @@ def test_validation_rejects_before_any_hip_call():
     assert S(0, 1, 128, 128, ctypes.byref(n)) == INVALID
     assert S(1, 1, 0, 128, ctypes.byref(n)) == INVALID
     assert S(1, 1, 128, 64, ctypes.byref(n)) == UNSUPPORTED
+    X = lib.kq_attn_mxfp4_fwd                   # the attention checks, then the scales
+    assert X(fake, None, fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 0.1, fake, None, None, 0,
+             None) == INVALID
+    assert X(fake, fake, fake, ctypes.c_void_p(0x10002), fake, 1, 1, 1, 128, 128, 1.0, 0.1, fake,
+             None, None, 0, None) == INVALID
+    assert X(fake, fake, fake, fake, fake, 1, 1, 1, 128, 64, 1.0, 0.1, fake, None, None, 0,
+             None) == UNSUPPORTED
+    assert X(fake, fake, fake, fake, fake, 1, 1, 1, 128, 128, 0.0, 0.1, fake, None, None, 0,
+             None) == INVALID
+    assert X(fake, fake, None, fake, fake, 1, 1, 1, 128, 128, 1.0, 0.1, fake, None, None, 0,
+             None) == INVALID
+    assert X(fake, fake, fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 0.1, fake, None, odd, 1 << 20,
+             None) == INVALID
     G8, G4 = lib.kq_gemm_fp8, lib.kq_gemm_mxfp4
     assert G8(fake, fake, 256, 256, 256, 1.0, 1.0, None, None) == INVALID
     assert G8(None, fake, 256, 256, 256, 1.0, 1.0, fake, None) == INVALID
