@@ -138,19 +138,25 @@ def attention_r3_mxfp4(q_codes, q_scales, k_codes, k_scales, v8, s_v, sm_scale, 
     return O, M, L
 
 
-def attention_r1(q8, k8, v8, s_q, s_k, s_v, sm_scale, amax_p=None):
+def attention_r1(q8, k8, v8, s_q, s_k, s_v, sm_scale, amax_p=None, rows=None):
     """R1: FakeQuantize on the normalized FP32 P with a calibrated per-tensor scale.
 
     P_ij = fl32(p_ij / l_i) with p, l as in R3 (the max shift cancels in P up to rounding);
     s_P = fl32(amax_P / 448) over the whole tensor; O = (E4M3(P / s_P) s_P) @ (E4M3(v) s_V).
-    Returns (O float32 [B, H, N, d], amax_p).
+    amax_P: the static calibrated maximum of P; None calibrates it on these inputs (max of P
+    over every row of every head, which needs rows=None).  rows: optional query rows to
+    evaluate (each row needs all keys, not the other rows).
+    Returns (O float32 [B, H, R, d], amax_p).
     """
     B, H, N, d = q8.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    if amax_p is None and len(rows) != N:
+        raise ValueError("calibrating amax_P needs every row")
     c1, _ = constants(s_q, s_k, s_v, sm_scale)
     Ps = []
     for b in range(B):
         for h in range(H):
-            raw = F.e4m3_decode(q8[b, h]) @ F.e4m3_decode(k8[b, h]).T
+            raw = F.e4m3_decode(q8[b, h, rows]) @ F.e4m3_decode(k8[b, h]).T
             t = F.fl32(raw * float(c1)).astype(np.float64)
             p = F.fl32(np.exp2(t - np.ceil(np.max(t, axis=1, keepdims=True))))
             l = F.fl32(np.sum(p.astype(np.float64), axis=1))
@@ -159,7 +165,7 @@ def attention_r1(q8, k8, v8, s_q, s_k, s_v, sm_scale, amax_p=None):
         amax_p = max(float(np.max(P)) for P in Ps)
     s_p = np.float32(np.float32(amax_p) / np.float32(P_SCALE))
     inv_p = np.float32(np.float32(P_SCALE) / np.float32(amax_p))
-    O = np.empty((B, H, N, d), np.float32)
+    O = np.empty((B, H, len(rows), d), np.float32)
     for i, P in enumerate(Ps):
         b, h = divmod(i, H)
         pq = F.e4m3_decode(F.e4m3_encode(P * inv_p)) * float(s_p)

@@ -206,6 +206,35 @@ def test_pipeline_tiny_against_unquantized_fp64():
     assert rel_l2(O1, ref) < 0.1
 
 
+def _pin_r1_closed_form():
+    """R1 on integer scores 0 (n_a keys) and -1 (n_b keys) with c1 = 1: p is 1 or 1/2, the
+    row sum l = n_a + n_b / 2, P = 1/l or 1/(2l), the calibrated amax_P = 1/l, and the FP8
+    codes of P / s_P are exactly 448 and 224, so O = (sum_a v + sum_b v / 2) s_V / l."""
+    rng = np.random.default_rng(12)
+    N, d = 80, 128
+    q8 = np.zeros((1, 1, N, d), np.uint8)
+    k8 = np.zeros((1, 1, N, d), np.uint8)
+    q8[..., 0] = 0x38                                     # q = e_0 (1.0)
+    grp_b = rng.random(N) < 0.4
+    k8[0, 0, grp_b, 0] = 0xB8                             # -1.0: score -1
+    v8 = _codes((1, 1, N, d), 13, hi=0x60)
+    sm, s_v = np.float32(math.log(2.0)), np.float32(0.5)
+    O, amax_p = A.attention_r1(q8, k8, v8, 1.0, 1.0, s_v, sm)
+    n_a, n_b = int(np.sum(~grp_b)), int(np.sum(grp_b))
+    l = n_a + 0.5 * n_b
+    assert amax_p == float(np.float32(1.0 / l))
+    vv = F.e4m3_decode(v8[0, 0]) * float(s_v)
+    ref = (vv[~grp_b].sum(axis=0) + 0.5 * vv[grp_b].sum(axis=0)) / l
+    assert np.allclose(O[0, 0], np.broadcast_to(ref, O[0, 0].shape), rtol=1e-6, atol=0)
+    # the same rows evaluated alone with the same static amax_P
+    Os, _ = A.attention_r1(q8, k8, v8, 1.0, 1.0, s_v, sm, amax_p=amax_p, rows=np.array([3, 79]))
+    assert np.array_equal(Os[0, 0], O[0, 0, [3, 79]])
+
+
+def test_r1_closed_form():
+    _pin_r1_closed_form()
+
+
 def test_pipeline_sampled_rows_equal_full_rows():
     qz = P.quantize_inputs(*W.qkv_bits(1))
     O, M, l = P.attention(qz)

@@ -84,7 +84,40 @@ def _unpack_ignoring_scales(codes, scales, block=32):
     return F.e2m1_decode(c)                                          # planted: no 2^e
 
 
+def _r1_variant(normalize_p: bool, amax_of_normalized: bool):
+    def r1(q8, k8, v8, s_q, s_k, s_v, sm_scale, amax_p=None, rows=None):
+        B, H, N, d = q8.shape
+        rows = np.arange(N) if rows is None else np.asarray(rows)
+        c1, _ = A.constants(s_q, s_k, s_v, sm_scale)
+        Ps, ps = [], []
+        for b in range(B):
+            for h in range(H):
+                raw = F.e4m3_decode(q8[b, h, rows]) @ F.e4m3_decode(k8[b, h]).T
+                t = F.fl32(raw * float(c1)).astype(np.float64)
+                p = F.fl32(np.exp2(t - np.ceil(np.max(t, axis=1, keepdims=True))))
+                l = F.fl32(np.sum(p.astype(np.float64), axis=1))
+                ps.append(p)
+                Ps.append(p / l[:, None] if normalize_p else p)
+        if amax_p is None:
+            amax_p = max(float(np.max(P)) for P in (Ps if amax_of_normalized else ps))
+        s_p = np.float32(np.float32(amax_p) / np.float32(448))
+        inv_p = np.float32(np.float32(448) / np.float32(amax_p))
+        O = np.empty((B, H, len(rows), d), np.float32)
+        for i, P in enumerate(Ps):
+            b, h = divmod(i, H)
+            pq = F.e4m3_decode(F.e4m3_encode(P * inv_p)) * float(s_p)
+            O[b, h] = F.fl32(pq @ (F.e4m3_decode(v8[b, h]) * float(np.float32(s_v))))
+        return O, amax_p
+    return r1
+
+
 MUTATIONS = {
+    "r1 without the 1/l normalization": (
+        lambda mp: mp.setattr(A, "attention_r1", _r1_variant(False, False)),
+        [TA._pin_r1_closed_form]),
+    "r1 amax_P calibrated on the unnormalized p": (
+        lambda mp: mp.setattr(A, "attention_r1", _r1_variant(True, False)),
+        [TA._pin_r1_closed_form]),
     "mxfp4 attention with 16-element scale blocks": (
         lambda mp: mp.setattr(Qz, "fp4_unpack", _unpack_block_16),
         [TA._pin_r3_mxfp4_equals_fp8_r3]),
