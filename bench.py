@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--native-fp4", action="store_true",
                     help="FP4 workloads: BMM1 on the FP4 Q, K (E2M1 + E8M0) instead of their "
                          "FP8 re-quantization")
+    ap.add_argument("--p-reading", choices=["r3", "r1"], default="r3",
+                    help="r1: the literal FakeQuantize of the normalized P, two passes, with "
+                         "amax_P calibrated offline")
     ap.add_argument("--gemm", choices=["fp8", "mxfp4"], default=None,
                     help="time a projection GEMM instead of the attention step")
     ap.add_argument("--gemm-shape", choices=["qkv", "out"], default="qkv")
@@ -272,7 +275,8 @@ def main():
         print(json.dumps({"error": "--native-fp4 needs an FP4 workload (--config 4 or 5)"}))
         sys.exit(2)
     m = QuantizedSDPA(c.B, c.H, c.N, c.d, mode=c.mode,
-                      positions=W.positions(c) if c.rope else None, native_fp4=args.native_fp4)
+                      positions=W.positions(c) if c.rope else None, native_fp4=args.native_fp4,
+                      p_reading=args.p_reading)
     m.calibrate(q, k, v)                     # offline static calibration, not timed
     stream = torch.cuda.current_stream()
 
@@ -338,15 +342,15 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": c.name, "B": c.B, "H": c.H, "N": c.N, "d": c.d, "mode": c.mode,
-                   "bmm1": "mxfp4" if args.native_fp4 else "fp8",
+                   "bmm1": "mxfp4" if args.native_fp4 else "fp8", "p_reading": args.p_reading,
                    "step": ("FP4 quantize Q,K,V (V then FP8) + attention with MXFP4 BMM1"
                             if args.native_fp4 else
                             "quantize Q,K,V to FP8 + fused attention (static scales)")},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": traffic_bytes() if args.config == 3 and not args.native_fp4
-                     else None},
+                     "traffic": traffic_bytes() if (args.config == 3 and not args.native_fp4
+                                                    and args.p_reading == "r3") else None},
         "pct_fp8_peak_step": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "attention_ms": round(attn_ms, 4),
         "quantize_ms": round(quant_ms, 4),

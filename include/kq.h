@@ -178,6 +178,33 @@ kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
                             float* o_f32, float* row_stats_or_null, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* Literal FakeQuantize of the normalized P ("R1"; blog bullet 4 and Fig. 4 read as a
+ * FakeQuantize node on the FP32 softmax output with a calibrated per-tensor scale), two
+ * passes over the keys, no key split:
+ *   pass 1: M = ceil(max t), l = sum exp2(t - M) per row (t as in kq_attn_quant_fwd);
+ *   pass 2: P = exp2(t - M) / l, codes = E4M3(P * 448 / amax_P) saturated at 448,
+ *           O = (sum codes E4M3(v)) * (amax_P / 448) * s_v.
+ * amax_P is the static calibrated maximum of P over the tensor (kq_attn_r1_amax).
+ * Same arguments and rules as kq_attn_quant_fwd.  row_stats4: device float32 [B*H][N][4]
+ * (16-byte aligned), written by pass 1 as (M, l, max_j exp2(t - M), 0) per row. */
+
+/* Pass 1 alone (calibration): fills row_stats4, writes no output. */
+kq_status kq_attn_r1_stats(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                           int v_layout, int B, int H, int N, int d, float s_q, float s_k,
+                           float s_v, float sm_scale, float* row_stats4, hipStream_t stream);
+
+/* amax_dev[0] = max(amax_dev[0], max over `rows` rows of row_stats4 of fl32(max p / l)): the
+ * largest normalized probability.  The caller zero-initializes amax_dev for a fresh
+ * calibration; rows = B*H*N. */
+kq_status kq_attn_r1_amax(const float* row_stats4, int64_t rows, float* amax_dev,
+                          hipStream_t stream);
+
+/* Both passes with the static amax_P (finite, > 0); o_f32 as kq_attn_quant_fwd. */
+kq_status kq_attn_r1_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, int v_layout,
+                         int B, int H, int N, int d, float s_q, float s_k, float s_v,
+                         float sm_scale, float amax_p, float* o_f32, float* row_stats4,
+                         hipStream_t stream);
+
 /* Quantized projection GEMMs: C = A B^T for the linear layers around the attention, with
  * per-tensor FP8 (W8A8) or per-block FP4 post-training quantization of both operands (blog
  * section "Workflow and Quantization", the quantization config and its PTQ paragraph).

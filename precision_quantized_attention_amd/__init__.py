@@ -21,7 +21,8 @@ __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSE
            "kq_status_string", "kq_vt_ld", "kq_fp8_scales_from_amax", "kq_rope3_table",
            "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
            "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws",
-           "kq_attn_mxfp4_fwd", "kq_gemm_fp8", "kq_gemm_mxfp4"]
+           "kq_attn_mxfp4_fwd", "kq_attn_r1_stats", "kq_attn_r1_amax", "kq_attn_r1_fwd",
+           "kq_gemm_fp8", "kq_gemm_mxfp4"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_LAYOUT_ROWS = 0
@@ -58,6 +59,9 @@ _SIGNATURES = {
                               ctypes.c_size_t, _P], _I),
     "kq_attn_mxfp4_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P,
                            ctypes.c_size_t, _P], _I),
+    "kq_attn_r1_stats": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P], _I),
+    "kq_attn_r1_amax": ([_P, _I64, _P, _P], _I),
+    "kq_attn_r1_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _F, _P, _P, _P], _I),
     "kq_gemm_fp8": ([_P, _P, _I64, _I64, _I64, _F, _F, _P, _P], _I),
     "kq_gemm_mxfp4": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
 }
@@ -271,6 +275,53 @@ def kq_attn_mxfp4_fwd(q_codes, q_scales, k_codes, k_scales, v8t, s_v: float, sm_
         _dev(v8t, torch.uint8, "v8"), v_layout, B, H, N, d, float(s_v), float(sm_scale),
         _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"), ws, nbytes,
         _stream(stream)), "kq_attn_mxfp4_fwd")
+
+
+def _attn_shapes(q8, k8, v8t, v_layout, o=None):
+    B, H, N, d = q8.shape
+    if tuple(k8.shape) != (B, H, N, d) or (o is not None and tuple(o.shape) != (B, H, N, d)):
+        raise KQError("k8 and o must match q8's shape")
+    if v_layout == KQ_LAYOUT_TRANSPOSED and v8t.numel() != B * H * d * kq_vt_ld(N):
+        raise KQError("v8t must be [B*H, d, kq_vt_ld(N)]")
+    return B, H, N, d
+
+
+def kq_attn_r1_stats(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float,
+                     row_stats4, v_layout: int = KQ_LAYOUT_TRANSPOSED, stream=None):
+    """First pass of R1: row_stats4 (float32 [B, H, N, 4]) = (M, l, max p, 0) per row."""
+    import torch
+    B, H, N, d = _attn_shapes(q8, k8, v8t, v_layout)
+    if row_stats4.numel() != B * H * N * 4:
+        raise KQError("row_stats4 must be [B, H, N, 4]")
+    _check(load().kq_attn_r1_stats(
+        _dev(q8, torch.uint8, "q8"), _dev(k8, torch.uint8, "k8"), _dev(v8t, torch.uint8, "v8"),
+        v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
+        _dev(row_stats4, torch.float32, "row_stats4"), _stream(stream)), "kq_attn_r1_stats")
+
+
+def kq_attn_r1_amax(row_stats4, amax, stream=None):
+    """amax[0] = max(amax[0], largest normalized probability in row_stats4)."""
+    import torch
+    if row_stats4.numel() % 4 or amax.numel() != 1:
+        raise KQError("row_stats4 must be [..., 4] and amax one float32")
+    _check(load().kq_attn_r1_amax(_dev(row_stats4, torch.float32, "row_stats4"),
+                                  row_stats4.numel() // 4, _dev(amax, torch.float32, "amax"),
+                                  _stream(stream)), "kq_attn_r1_amax")
+
+
+def kq_attn_r1_fwd(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float,
+                   amax_p: float, o, row_stats4, v_layout: int = KQ_LAYOUT_TRANSPOSED,
+                   stream=None):
+    """R1 attention (both passes) with the static amax_P; row_stats4 float32 [B, H, N, 4]."""
+    import torch
+    B, H, N, d = _attn_shapes(q8, k8, v8t, v_layout, o)
+    if row_stats4.numel() != B * H * N * 4:
+        raise KQError("row_stats4 must be [B, H, N, 4]")
+    _check(load().kq_attn_r1_fwd(
+        _dev(q8, torch.uint8, "q8"), _dev(k8, torch.uint8, "k8"), _dev(v8t, torch.uint8, "v8"),
+        v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
+        float(amax_p), _dev(o, torch.float32, "o"),
+        _dev(row_stats4, torch.float32, "row_stats4"), _stream(stream)), "kq_attn_r1_fwd")
 
 
 def kq_gemm_fp8(a8, b8, s_a: float, s_b: float, c, stream=None):

@@ -152,6 +152,7 @@ struct Geo {
   int n, g;
   int kbase;                         // first key of the workgroup's key range
   float c1;
+  float m_fix, lb_fix;               // R1 pass 2: the row's offset M and log2(inv_p / l)
 };
 
 // BMM1's Q operand, held in registers for the whole key loop.
@@ -351,11 +352,35 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
 // 2^(M_kb - m_ref) as its scale: no accumulator rescale when the running maximum grows.
 // Codes differ from full-row ones by exact powers of two, which E4M3 rounding preserves in its
 // normal range.  Outputs the block offsets d0, d1 (relative to m_ref) and the scale byte.
+//
+// kR1 (second pass of the literal FakeQuantize of the normalized P): the row's offset M and
+// sum l are known from the first pass, so every block uses M, the scale bytes stay 1.0 and
+// the value quantized is p inv_p / l = exp2(t - M + log2(inv_p / l)), saturated at 448.
+template <bool kR1>
 __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float mx1,
                                            float& m_ref, float& m_top, float& lsum,
                                            v16f (&o)[4], int& pscale, float& d0o, float& d1o,
-                                           const Geo& G) {
+                                           float& rmax, const Geo& G) {
   const float c1 = G.c1;
+  if constexpr (kR1) {
+    m_ref = m_top = G.m_fix;
+    pscale = 127;
+    d0o = d1o = 0.0f;
+    const float bias = G.lb_fix - G.m_fix;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int kb = h >> 1, i0 = 8 * (h & 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[kb][i0 + i] = __builtin_fmaf(s[kb][i0 + i], c1, bias);
+      KQ_FENCE();
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        s[kb][i0 + i] = fminf(__builtin_amdgcn_exp2f(s[kb][i0 + i]), 448.0f);
+    }
+    asm volatile("" ::"v"(s[0]), "v"(s[1]));
+    return;
+  }
+  rmax = fmaxf(rmax, fmaxf(mx0, mx1));       // the row's largest raw score (first pass of R1)
   float mb0 = ceilf(mx0 * c1), mb1 = ceilf(mx1 * c1);
   if (j == 0) {                    // row reference: the row's offset on the first tile
     const float mr = fmaxf(mb0, mb1);
@@ -400,7 +425,7 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
   asm volatile("" ::"v"(s[0]), "v"(s[1]));
 }
 
-template <bool kFP4>
+template <bool kFP4, bool kR1>
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int nqb) {
   // bf16 K tiles, or packed E2M1 K tiles + scales (kFP4)
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * (kFP4 ? kK4Stage : kKStage)];
@@ -497,6 +522,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     G.g = g;
     G.kbase = __builtin_amdgcn_readfirstlane(t_begin * kBN);
     G.c1 = a.c1;
+    G.m_fix = 0.0f;
+    G.lb_fix = 0.0f;
+    if constexpr (kR1) {
+      // (M, l) of this row from the first pass; rows past N keep M = 0, l = 1
+      const __amdgpu_buffer_rsrc_t sr =
+          make_rsrc(a.r1_stats + (int64_t)bh * N * 4, (uint32_t)N * 16);
+      const u32x4 st = __builtin_amdgcn_raw_buffer_load_b128(sr, (uint32_t)q * 16, 0, 0);
+      const float m = __uint_as_float(st[0]), l = __uint_as_float(st[1]);
+      const bool ok = l > 0.0f;
+      G.m_fix = ok ? m : 0.0f;
+      G.lb_fix = log2f(a.r1_inv_p / (ok ? l : 1.0f));
+    }
   }
 
   v16f o[4];
@@ -512,6 +549,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   float d0 = 0.0f, d1 = 0.0f;  // block offsets of the last softmaxed tile, relative to m_ref
   float m_ref = 0.0f;        // per-row reference offset (integer-valued), set on tile 0
   float m_top = -INFINITY;   // largest block offset seen (for the row statistics)
+  float rmax = -INFINITY;    // largest raw score of the row (first pass of R1)
   float lsum = 0.0f;         // partial row sum of 448 p * 2^(M_kb - m_ref) over this lane's keys
   const int ntiles = __builtin_amdgcn_readfirstlane(t_end - t_begin);   // tiles of this range
   const int grp = __builtin_amdgcn_readfirstlane(w >> 2);    // 0: waves 0-3, 1: waves 4-7 (one per SIMD each)
@@ -535,12 +573,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   for (int j = 0;; j += 2) {
     mfma_phase<kFP4>(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
-    if (j < ntiles) valu_phase(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, G);
+    if (j < ntiles) valu_phase<kR1>(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
     if (j + 1 > ntiles) break;
     mfma_phase<kFP4>(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
-    if (j + 1 < ntiles) valu_phase(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, G);
+    if (j + 1 < ntiles) valu_phase<kR1>(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
     if (j + 2 > ntiles) break;
   }
@@ -565,8 +603,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     }
     return;
   }
-  const float scale = a.s_v / ltot;
-  if (q < N) {
+  // R1 second pass: P was normalized before quantization, O = acc s_P s_V
+  const float scale = kR1 ? a.r1_s_p * a.s_v : a.s_v / ltot;
+  if (q < N && a.o != nullptr) {
     float* op = a.o + ((int64_t)bh * N + q) * kD;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -576,10 +615,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
                                o[c][4 * i4 + 2] * scale, o[c][4 * i4 + 3] * scale);
         *reinterpret_cast<float4*>(op + 32 * c + 8 * i4 + 4 * g) = v;
       }
-    if (a.stats != nullptr && g == 0) {
-      // (M, l) with l relative to the row's M
-      float2 st = make_float2(m_row, __builtin_amdgcn_ldexpf(ltot * (1.0f / 448.0f), (int)(m_ref - m_row)));
-      *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * N + q) * 2) = st;
+  }
+  if (!kR1 && q < N && g == 0) {
+    // (M, l) with l relative to the row's M
+    const float lrel = __builtin_amdgcn_ldexpf(ltot * (1.0f / 448.0f), (int)(m_ref - m_row));
+    if (a.stats != nullptr)
+      *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * N + q) * 2) = make_float2(m_row, lrel);
+    if (a.stats4 != nullptr) {
+      // first pass of R1: also the row's largest p = exp2(max t - M)
+      const float pmax = exp2f(rmax * a.c1 - m_row);
+      *reinterpret_cast<float4*>(a.stats4 + ((int64_t)bh * N + q) * 4) =
+          make_float4(m_row, lrel, pmax, 0.0f);
     }
   }
 }
@@ -626,15 +672,40 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
   }
 }
 
+// amax_P of R1 from first-pass row statistics: amax[0] = max(amax[0], max over rows of
+// fl32(pmax / l)), the largest normalized probability.  One workgroup.
+__global__ void __launch_bounds__(1024) r1_amax_kernel(const float* st, int64_t rows, float* amax) {
+  __shared__ float red[1024];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < rows; i += 1024) {
+    const float4 v = reinterpret_cast<const float4*>(st)[i];
+    if (v.y > 0.0f) m = fmaxf(m, v.z / v.y);
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) amax[0] = fmaxf(amax[0], red[0]);
+}
+
 }  // namespace
+
+hipError_t launch_r1_amax(const float* row_stats4, int64_t rows, float* amax, hipStream_t stream) {
+  hipLaunchKernelGGL(r1_amax_kernel, dim3(1), dim3(1024), 0, stream, row_stats4, rows, amax);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream) {
   const int nqb = (p.n + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)p.nfull + (int64_t)p.rem * p.split;
-  if (p.q_scales != nullptr)
-    hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+  if (p.r1_stats != nullptr)
+    hipLaunchKernelGGL((attn_fp8_kernel<false, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+  else if (p.q_scales != nullptr)
+    hipLaunchKernelGGL((attn_fp8_kernel<true, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
   else
-    hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+    hipLaunchKernelGGL((attn_fp8_kernel<false, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split == 0) return e;
   const int64_t cblocks = ((int64_t)p.rem * kBM * 32 + 255) / 256;

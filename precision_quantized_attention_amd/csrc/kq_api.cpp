@@ -90,6 +90,9 @@ kq_status attn_params(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, i
   p->rem = 0;
   p->split = 0;
   p->ws = nullptr;
+  p->stats4 = nullptr;
+  p->r1_stats = nullptr;
+  p->r1_inv_p = p->r1_s_p = 0.0f;
   return KQ_OK;
 }
 
@@ -312,6 +315,49 @@ kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
   p.k_scales = k_scales;
   const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
   if (sw != KQ_OK) return sw;
+  return from_hip(kq::launch_attn_fp8(p, stream));
+}
+
+kq_status kq_attn_r1_stats(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                           int v_layout, int B, int H, int N, int d, float s_q, float s_k,
+                           float s_v, float sm_scale, float* row_stats4, hipStream_t stream) {
+  kq::AttnParams p;
+  // row_stats4 stands in for the output in the shared checks (the first pass writes no O)
+  const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
+                                   row_stats4, nullptr, &p);
+  if (st != KQ_OK) return st;
+  p.o = nullptr;
+  p.stats4 = row_stats4;
+  return from_hip(kq::launch_attn_fp8(p, stream));
+}
+
+kq_status kq_attn_r1_amax(const float* row_stats4, int64_t rows, float* amax_dev,
+                          hipStream_t stream) {
+  if (row_stats4 == nullptr || amax_dev == nullptr || rows < 1) return KQ_ERR_INVALID_ARG;
+  if (!aligned(row_stats4, 16) || !aligned(amax_dev, 4)) return KQ_ERR_INVALID_ARG;
+  return from_hip(kq::launch_r1_amax(row_stats4, rows, amax_dev, stream));
+}
+
+kq_status kq_attn_r1_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, int v_layout,
+                         int B, int H, int N, int d, float s_q, float s_k, float s_v,
+                         float sm_scale, float amax_p, float* o_f32, float* row_stats4,
+                         hipStream_t stream) {
+  if (!finite_pos(amax_p) || row_stats4 == nullptr || !aligned(row_stats4, 16))
+    return KQ_ERR_INVALID_ARG;
+  const float s_p = amax_p / 448.0f, inv_p = 448.0f / amax_p;
+  if (!finite_pos(s_p) || !finite_pos(inv_p)) return KQ_ERR_INVALID_ARG;
+  kq::AttnParams p;
+  const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
+                                   o_f32, nullptr, &p);
+  if (st != KQ_OK) return st;
+  kq::AttnParams p1 = p;
+  p1.o = nullptr;
+  p1.stats4 = row_stats4;
+  const hipError_t e = kq::launch_attn_fp8(p1, stream);
+  if (e != hipSuccess) return KQ_ERR_HIP;
+  p.r1_stats = row_stats4;
+  p.r1_inv_p = inv_p;
+  p.r1_s_p = s_p;
   return from_hip(kq::launch_attn_fp8(p, stream));
 }
 

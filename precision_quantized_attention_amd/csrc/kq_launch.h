@@ -40,6 +40,11 @@ struct AttnParams {
   int rem;
   int split;
   float* ws;              // [rem * split][256][128] partial acc, then [rem * split][256][4] stats
+  // Literal FakeQuantize of the normalized P (R1), two passes, no key split.
+  float* stats4;          // first pass: [BH][N][4] = (M, l, max p, 0) per row, or nullptr
+  const float* r1_stats;  // second pass: the first pass's stats4 (nullptr: not R1)
+  float r1_inv_p;         // 448 / amax_P
+  float r1_s_p;           // amax_P / 448
 };
 
 // Query rows per attention workgroup (the unit of the split).
@@ -51,6 +56,8 @@ inline size_t attn_workspace_bytes(int rem, int split) {
 }
 
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream);
+
+hipError_t launch_r1_amax(const float* row_stats4, int64_t rows, float* amax, hipStream_t stream);
 
 struct GemmParams {
   const uint8_t* a;         // [M][K] E4M3 codes, or [M][K/2] packed E2M1 codes

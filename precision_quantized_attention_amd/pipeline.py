@@ -23,6 +23,7 @@ import numpy as np
 import torch
 
 from . import (KQ_LAYOUT_TRANSPOSED, kq_amax_calibrate, kq_attn_mxfp4_fwd, kq_attn_quant_fwd_ws,
+               kq_attn_r1_amax, kq_attn_r1_fwd, kq_attn_r1_stats,
                kq_attn_workspace_size,
                kq_fp8_scales_from_amax, kq_quantize_fp4_block, kq_quantize_fp8_tensor,
                kq_rope3_table, kq_vt_ld)
@@ -47,15 +48,22 @@ class QuantizedSDPA:
     Q and K before FP4 quantization (FP4 mode only).
     native_fp4 (FP4 mode only): BMM1 multiplies the FP4 Q, K directly (E2M1 + E8M0 on the
     matrix cores) instead of their per-tensor FP8 re-quantization; V still goes FP4 -> FP8.
+    p_reading "r3" (default): the one-pass reading (static 1/448 scale on exp2(t - M), row sum
+    after BMM2).  "r1": the literal FakeQuantize of the normalized P with a calibrated
+    per-tensor amax_P, two passes (FP8 BMM1 only).
     """
 
     def __init__(self, B, H, N, d=128, mode="fp8", positions=None, device="cuda",
-                 sm_scale=None, want_stats=False, native_fp4=False):
+                 sm_scale=None, want_stats=False, native_fp4=False, p_reading="r3"):
         if mode not in ("fp8", "fp4"):
             raise ValueError(mode)
         if native_fp4 and mode != "fp4":
             raise ValueError("native_fp4 needs mode 'fp4'")
         self.native_fp4 = native_fp4
+        if p_reading not in ("r3", "r1") or (p_reading == "r1" and native_fp4):
+            raise ValueError(p_reading)
+        self.p_reading = p_reading
+        self.amax_p = None
         if positions is not None and mode != "fp4":
             raise ValueError("the rotary embedding is fused into the FP4 quantizer")
         self.B, self.H, self.N, self.d, self.mode = B, H, N, d, mode
@@ -101,7 +109,23 @@ class QuantizedSDPA:
         a = amax.cpu().numpy()
         self.amax = {n: float(a[i]) for i, n in enumerate("qkv")}
         self.scales = {n: kq_fp8_scales_from_amax(a[i]) for i, n in enumerate("qkv")}
+        if self.p_reading == "r1":
+            # amax_P: the largest normalized probability over the calibration inputs
+            self.quantize(q, k, v)
+            b = self.buf
+            st = self._r1_stats()
+            kq_attn_r1_stats(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
+                             self.scales["v"][0], self.sm_scale, st)
+            am = torch.zeros(1, dtype=torch.float32, device=self.device)
+            kq_attn_r1_amax(st, am)
+            self.amax_p = float(am.item())
         return self.scales
+
+    def _r1_stats(self):
+        if getattr(self, "_st4", None) is None:
+            self._st4 = torch.empty((self.B, self.H, self.N, 4), dtype=torch.float32,
+                                    device=self.device)
+        return self._st4
 
     def quantize(self, q, k, v):
         """Per-forward quantization of Q, K, V into the FP8 attention inputs."""
@@ -133,7 +157,11 @@ class QuantizedSDPA:
             self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=self.device)
                               if nbytes else False)
         ws = self.workspace if self.workspace is not False else None
-        if self.native_fp4:
+        if self.p_reading == "r1":
+            kq_attn_r1_fwd(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
+                           self.scales["v"][0], self.sm_scale, self.amax_p, b.o,
+                           self._r1_stats())
+        elif self.native_fp4:
             (qc, qs), (kc, ks) = b.fp4["q"], b.fp4["k"]
             kq_attn_mxfp4_fwd(qc, qs, kc, ks, b.v8t, self.scales["v"][0], self.sm_scale, b.o,
                               ws, row_stats=b.stats)

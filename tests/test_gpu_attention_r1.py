@@ -1,0 +1,155 @@
+"""GPU parity of the literal FakeQuantize of the normalized P (R1: kq_attn_r1_stats,
+kq_attn_r1_amax, kq_attn_r1_fwd) against the oracle's attention_r1.
+
+Calibration (first pass + amax reduction) must reproduce the oracle's amax_P (within 1e-5),
+and with the same static amax_P the two-pass output must stay within rel-L2 1e-2 and, per
+element, max-abs 5e-2 plus the effect of near-ties: R1 quantizes x = P / s_P to E4M3, and
+where x lies within 1e-5 (relative) of an E4M3 rounding midpoint, the float32 evaluation on
+the device (BMM1 summed in float32, exp2 of a shifted argument) may round it to either
+neighbour.  Each such element j of row i may move O[i, d] by the code gap times s_P |v_jd| s_V;
+the sum of those terms is added to the row's allowance.  At the Kontext size the oracle cannot
+hold every row's P, so both sides take the same static amax_P and the oracle evaluates sampled
+rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import precision_quantized_attention_amd as kq
+import workloads as W
+from kq_testutil import MAX_ABS_TOL, REL_L2_TOL, max_abs, rel_l2, sample_rows, to_dev
+from oracle import attention as A
+from oracle import formats as F
+from oracle import pipeline as OP
+from precision_quantized_attention_amd.pipeline import QuantizedSDPA
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantized(bits):
+    B, H, N, d = bits[0].shape
+    x = [to_dev(b) for b in bits]
+    m = QuantizedSDPA(B, H, N, d)
+    m.calibrate(*x)
+    m.quantize(*x)
+    torch.cuda.synchronize()
+    return m
+
+
+def _r1_gpu(m, amax_p=None):
+    b = m.buf
+    B, H, N, d = b.q8.shape
+    (sq, _), (sk, _), (sv, _) = m.scales["q"], m.scales["k"], m.scales["v"]
+    st = torch.empty((B, H, N, 4), dtype=torch.float32, device="cuda")
+    if amax_p is None:
+        am = torch.zeros(1, dtype=torch.float32, device="cuda")
+        kq.kq_attn_r1_stats(b.q8, b.k8, b.v8t, sq, sk, sv, m.sm_scale, st)
+        kq.kq_attn_r1_amax(st, am)
+        amax_p = float(am.item())
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    kq.kq_attn_r1_fwd(b.q8, b.k8, b.v8t, sq, sk, sv, m.sm_scale, amax_p, o, st)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), st.cpu().numpy(), amax_p
+
+
+_E4M3_POS = np.unique(F.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))   # 0 .. 448
+_MID = (_E4M3_POS[1:] + _E4M3_POS[:-1]) / 2
+_GAP = _E4M3_POS[1:] - _E4M3_POS[:-1]
+
+
+def _tie_allowance(q8, k8, v8, s_q, s_k, s_v, sm, amax_p, rows, rel=1e-5):
+    """[B, H, R, d] allowance: sum over near-tie elements j of gap_j s_P |v_jd| s_V, with x
+    evaluated by the oracle's definition (R1, module docstring of oracle/attention.py)."""
+    B, H, N, d = q8.shape
+    c1, _ = A.constants(s_q, s_k, s_v, sm)
+    s_p = float(np.float32(np.float32(amax_p) / np.float32(448.0)))
+    inv_p = np.float32(np.float32(448.0) / np.float32(amax_p))
+    out = np.zeros((B, H, len(rows), d))
+    for b in range(B):
+        for h in range(H):
+            raw = F.e4m3_decode(q8[b, h, rows]) @ F.e4m3_decode(k8[b, h]).T
+            t = F.fl32(raw * float(c1)).astype(np.float64)
+            p = F.fl32(np.exp2(t - np.ceil(np.max(t, axis=1, keepdims=True))))
+            l = F.fl32(np.sum(p.astype(np.float64), axis=1))
+            x = (p / l[:, None] * inv_p).astype(np.float64)
+            i = np.clip(np.searchsorted(_MID, x), 1, len(_MID)) - 1
+            near = np.minimum(np.abs(x - _MID[i]), np.abs(x - _MID[np.minimum(i + 1, len(_MID) - 1)]))
+            gap = np.where(np.abs(x - _MID[i]) <= np.abs(x - _MID[np.minimum(i + 1, len(_MID) - 1)]),
+                           _GAP[i], _GAP[np.minimum(i + 1, len(_MID) - 1)])
+            w = np.where(near <= rel * np.maximum(x, 1e-30), gap, 0.0) * s_p * float(s_v)
+            out[b, h] = w @ np.abs(F.e4m3_decode(v8[b, h]))
+    return out
+
+
+def _compare(o_gpu, o_ref, label, allowance=0.0):
+    e, a = rel_l2(o_gpu, o_ref), max_abs(o_gpu, o_ref)
+    excess = float(np.max(np.abs(np.asarray(o_gpu, np.float64) - o_ref) - allowance))
+    print(f"{label}: rel_l2 {e:.3e} max_abs {a:.3e} (|O| max {np.abs(o_ref).max():.3g}; "
+          f"largest near-tie allowance {np.max(allowance):.3g}, max excess over it {excess:.3g})",
+          flush=True)
+    assert e <= REL_L2_TOL, (label, e)
+    assert excess <= MAX_ABS_TOL, (label, a, excess)
+
+
+@pytest.mark.parametrize("H,N,outliers", [(2, 256, False), (2, 1, False), (1, 65, True),
+                                          (2, 300, True), (3, 1000, True), (1, 2560, True)])
+def test_r1_calibrated_matches_oracle(H, N, outliers):
+    print(f"r1 H={H} N={N} outliers={outliers}", flush=True)
+    bits = [W.random_bits(1, H, N, 128, seed=1500 + 7 * N + t, outliers=outliers)
+            for t in range(3)]
+    m = _quantized(bits)
+    _, st, amax_gpu = _r1_gpu(m)                       # calibration on the device
+    qz = OP.quantize_inputs(*bits)
+    args = (qz.codes["q"], qz.codes["k"], qz.codes["v"], qz.scale["q"][0], qz.scale["k"][0],
+            qz.scale["v"][0], m.sm_scale)
+    O, amax_ref = A.attention_r1(*args)
+    print(f"amax_P gpu {amax_gpu:.9g} oracle {amax_ref:.9g}", flush=True)
+    assert abs(amax_gpu - amax_ref) <= 1e-5 * amax_ref
+    o, _, _ = _r1_gpu(m, amax_ref)                     # forward with the same static amax_P
+    _compare(o, O, f"r1 H={H} N={N}", _tie_allowance(*args, amax_ref, np.arange(N)))
+    # first-pass statistics against the oracle's R3 row statistics (same M and l)
+    _, M, L = A.attention_r3(qz.codes["q"], qz.codes["k"], qz.codes["v"], qz.scale["q"][0],
+                             qz.scale["k"][0], qz.scale["v"][0], m.sm_scale)
+    assert np.all(np.abs(st[..., 0] - M) <= 1)
+    assert np.allclose(st[..., 1].astype(np.float64) * np.exp2(st[..., 0]),
+                       L.astype(np.float64) * np.exp2(M), rtol=1e-4)
+    assert np.all((st[..., 2] > 0.5) & (st[..., 2] <= 1.0))
+
+
+def test_r1_static_amax_with_saturation():
+    """A static amax_P below the tensor's true maximum: both sides saturate the largest P
+    codes at 448."""
+    print("r1 saturation", flush=True)
+    bits = [W.random_bits(1, 2, 400, 128, seed=1700 + t, outliers=True) for t in range(3)]
+    m = _quantized(bits)
+    qz = OP.quantize_inputs(*bits)
+    _, amax_ref = A.attention_r1(qz.codes["q"], qz.codes["k"], qz.codes["v"], qz.scale["q"][0],
+                                 qz.scale["k"][0], qz.scale["v"][0], m.sm_scale)
+    amax_p = float(np.float32(amax_ref * 0.3))
+    o, _, _ = _r1_gpu(m, amax_p)
+    args = (qz.codes["q"], qz.codes["k"], qz.codes["v"], qz.scale["q"][0], qz.scale["k"][0],
+            qz.scale["v"][0], m.sm_scale)
+    O, _ = A.attention_r1(*args, amax_p=amax_p)
+    _compare(o, O, "r1 saturated", _tie_allowance(*args, amax_p, np.arange(400)))
+
+
+def test_r1_kontext_sampled_rows():
+    c = W.config(3)
+    print(f"r1 {c.name} sampled rows", flush=True)
+    bits = W.qkv_bits(3)
+    m = _quantized(bits)
+    amax_p = 0.0625                      # static calibrated value, given to both sides
+    o, st, _ = _r1_gpu(m, amax_p)
+    qz = OP.quantize_inputs(*bits)
+    rows = sample_rows(c.N, 16, seed=31)
+    heads = [(0, 0), (0, c.H - 1), (0, 11)]
+    sub = {n: np.stack([qz.codes[n][b, h] for b, h in heads])[None] for n in "qkv"}
+    args = (sub["q"], sub["k"], sub["v"], qz.scale["q"][0], qz.scale["k"][0], qz.scale["v"][0],
+            m.sm_scale)
+    O, _ = A.attention_r1(*args, amax_p=amax_p, rows=rows)
+    got = np.stack([o[b, h][rows] for b, h in heads])
+    _compare(got, O[0], "r1 kontext", _tie_allowance(*args, amax_p, rows)[0])
+    # reported: R1 against R3 on the same rows (the quantization noise the reading moves)
+    O3, _, _ = A.attention_r3(sub["q"], sub["k"], sub["v"], qz.scale["q"][0], qz.scale["k"][0],
+                              qz.scale["v"][0], m.sm_scale, rows=rows)
+    print(f"r1 vs r3 (oracle, same rows): rel_l2 {rel_l2(O[0], O3[0]):.3e}", flush=True)
