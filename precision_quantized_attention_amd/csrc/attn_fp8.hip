@@ -353,16 +353,17 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
 // Codes differ from full-row ones by exact powers of two, which E4M3 rounding preserves in its
 // normal range.  Outputs the block offsets d0, d1 (relative to m_ref) and the scale byte.
 //
-// kR1 (second pass of the literal FakeQuantize of the normalized P): the row's offset M and
-// sum l are known from the first pass, so every block uses M, the scale bytes stay 1.0 and
+// kMode 2 (second pass of the literal FakeQuantize of the normalized P): the row's offset M
+// and sum l are known from the first pass, so every block uses M, the scale bytes stay 1.0 and
 // the value quantized is p inv_p / l = exp2(t - M + log2(inv_p / l)), saturated at 448.
-template <bool kR1>
+// kMode 1 (its first pass) also tracks the row's largest raw score.
+template <int kMode>
 __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float mx1,
                                            float& m_ref, float& m_top, float& lsum,
                                            v16f (&o)[4], int& pscale, float& d0o, float& d1o,
                                            float& rmax, const Geo& G) {
   const float c1 = G.c1;
-  if constexpr (kR1) {
+  if constexpr (kMode == 2) {
     m_ref = m_top = G.m_fix;
     pscale = 127;
     d0o = d1o = 0.0f;
@@ -380,7 +381,7 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
     asm volatile("" ::"v"(s[0]), "v"(s[1]));
     return;
   }
-  rmax = fmaxf(rmax, fmaxf(mx0, mx1));       // the row's largest raw score (first pass of R1)
+  if constexpr (kMode == 1) rmax = fmaxf(rmax, fmaxf(mx0, mx1));   // the row's largest raw score
   float mb0 = ceilf(mx0 * c1), mb1 = ceilf(mx1 * c1);
   if (j == 0) {                    // row reference: the row's offset on the first tile
     const float mr = fmaxf(mb0, mb1);
@@ -425,8 +426,11 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
   asm volatile("" ::"v"(s[0]), "v"(s[1]));
 }
 
-template <bool kFP4, bool kR1>
+// kMode: 0 the one-pass attention; 1 the same plus the (M, l, max p) row statistics of R1's
+// first pass; 2 R1's second pass.
+template <bool kFP4, int kMode>
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int nqb) {
+  constexpr bool kR1 = kMode == 2;
   // bf16 K tiles, or packed E2M1 K tiles + scales (kFP4)
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * (kFP4 ? kK4Stage : kKStage)];
   __shared__ __attribute__((aligned(16))) uint8_t Vs[2 * kVStage];   // FP8 V^T tiles
@@ -573,12 +577,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   for (int j = 0;; j += 2) {
     mfma_phase<kFP4>(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
-    if (j < ntiles) valu_phase<kR1>(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
+    if (j < ntiles) valu_phase<kMode>(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
     if (j + 1 > ntiles) break;
     mfma_phase<kFP4>(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
-    if (j + 1 < ntiles) valu_phase<kR1>(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
+    if (j + 1 < ntiles) valu_phase<kMode>(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
     if (j + 2 > ntiles) break;
   }
@@ -621,7 +625,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     const float lrel = __builtin_amdgcn_ldexpf(ltot * (1.0f / 448.0f), (int)(m_ref - m_row));
     if (a.stats != nullptr)
       *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * N + q) * 2) = make_float2(m_row, lrel);
-    if (a.stats4 != nullptr) {
+    if (kMode == 1) {
       // first pass of R1: also the row's largest p = exp2(max t - M)
       const float pmax = exp2f(rmax * a.c1 - m_row);
       *reinterpret_cast<float4*>(a.stats4 + ((int64_t)bh * N + q) * 4) =
@@ -701,11 +705,13 @@ hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream) {
   const int nqb = (p.n + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)p.nfull + (int64_t)p.rem * p.split;
   if (p.r1_stats != nullptr)
-    hipLaunchKernelGGL((attn_fp8_kernel<false, true>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+  else if (p.stats4 != nullptr)
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
   else if (p.q_scales != nullptr)
-    hipLaunchKernelGGL((attn_fp8_kernel<true, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+    hipLaunchKernelGGL((attn_fp8_kernel<true, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
   else
-    hipLaunchKernelGGL((attn_fp8_kernel<false, false>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split == 0) return e;
   const int64_t cblocks = ((int64_t)p.rem * kBM * 32 + 255) / 256;
