@@ -186,12 +186,16 @@ kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
  *           O = (sum codes E4M3(v)) * (amax_P / 448) * s_v.
  * amax_P is the static calibrated maximum of P over the tensor (kq_attn_r1_amax).
  * Same arguments and rules as kq_attn_quant_fwd.  row_stats4: device float32 [B*H][N][4]
- * (16-byte aligned), written by pass 1 as (M, l, max_j exp2(t - M), 0) per row. */
+ * (16-byte aligned), written by pass 1 as (M, l, max_j exp2(t - M), 0) per row.  workspace:
+ * as kq_attn_quant_fwd_ws (NULL: no key split; size from kq_attn_workspace_size), used by each
+ * pass in turn; the partial results of the second pass share the row's M and merge by plain
+ * summation. */
 
 /* Pass 1 alone (calibration): fills row_stats4, writes no output. */
 kq_status kq_attn_r1_stats(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                            int v_layout, int B, int H, int N, int d, float s_q, float s_k,
-                           float s_v, float sm_scale, float* row_stats4, hipStream_t stream);
+                           float s_v, float sm_scale, float* row_stats4, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* amax_dev[0] = max(amax_dev[0], max over `rows` rows of row_stats4 of fl32(max p / l)): the
  * largest normalized probability.  The caller zero-initializes amax_dev for a fresh
@@ -203,7 +207,7 @@ kq_status kq_attn_r1_amax(const float* row_stats4, int64_t rows, float* amax_dev
 kq_status kq_attn_r1_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, int v_layout,
                          int B, int H, int N, int d, float s_q, float s_k, float s_v,
                          float sm_scale, float amax_p, float* o_f32, float* row_stats4,
-                         hipStream_t stream);
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Quantized projection GEMMs: C = A B^T for the linear layers around the attention, with
  * per-tensor FP8 (W8A8) or per-block FP4 post-training quantization of both operands (blog

@@ -59,9 +59,11 @@ _SIGNATURES = {
                               ctypes.c_size_t, _P], _I),
     "kq_attn_mxfp4_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P,
                            ctypes.c_size_t, _P], _I),
-    "kq_attn_r1_stats": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P], _I),
+    "kq_attn_r1_stats": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P,
+                          ctypes.c_size_t, _P], _I),
     "kq_attn_r1_amax": ([_P, _I64, _P, _P], _I),
-    "kq_attn_r1_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _F, _P, _P, _P], _I),
+    "kq_attn_r1_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _F, _P, _P, _P,
+                        ctypes.c_size_t, _P], _I),
     "kq_gemm_fp8": ([_P, _P, _I64, _I64, _I64, _F, _F, _P, _P], _I),
     "kq_gemm_mxfp4": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
 }
@@ -287,16 +289,20 @@ def _attn_shapes(q8, k8, v8t, v_layout, o=None):
 
 
 def kq_attn_r1_stats(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float,
-                     row_stats4, v_layout: int = KQ_LAYOUT_TRANSPOSED, stream=None):
-    """First pass of R1: row_stats4 (float32 [B, H, N, 4]) = (M, l, max p, 0) per row."""
+                     row_stats4, workspace=None, v_layout: int = KQ_LAYOUT_TRANSPOSED,
+                     stream=None):
+    """First pass of R1: row_stats4 (float32 [B, H, N, 4]) = (M, l, max p, 0) per row;
+    workspace as kq_attn_quant_fwd_ws (or None)."""
     import torch
     B, H, N, d = _attn_shapes(q8, k8, v8t, v_layout)
     if row_stats4.numel() != B * H * N * 4:
         raise KQError("row_stats4 must be [B, H, N, 4]")
+    nbytes = 0 if workspace is None else workspace.numel()
     _check(load().kq_attn_r1_stats(
         _dev(q8, torch.uint8, "q8"), _dev(k8, torch.uint8, "k8"), _dev(v8t, torch.uint8, "v8"),
         v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
-        _dev(row_stats4, torch.float32, "row_stats4"), _stream(stream)), "kq_attn_r1_stats")
+        _dev(row_stats4, torch.float32, "row_stats4"),
+        _opt(workspace, torch.uint8, "workspace"), nbytes, _stream(stream)), "kq_attn_r1_stats")
 
 
 def kq_attn_r1_amax(row_stats4, amax, stream=None):
@@ -310,9 +316,10 @@ def kq_attn_r1_amax(row_stats4, amax, stream=None):
 
 
 def kq_attn_r1_fwd(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float,
-                   amax_p: float, o, row_stats4, v_layout: int = KQ_LAYOUT_TRANSPOSED,
-                   stream=None):
-    """R1 attention (both passes) with the static amax_P; row_stats4 float32 [B, H, N, 4]."""
+                   amax_p: float, o, row_stats4, workspace=None,
+                   v_layout: int = KQ_LAYOUT_TRANSPOSED, stream=None):
+    """R1 attention (both passes) with the static amax_P; row_stats4 float32 [B, H, N, 4];
+    workspace as kq_attn_quant_fwd_ws (or None)."""
     import torch
     B, H, N, d = _attn_shapes(q8, k8, v8t, v_layout, o)
     if row_stats4.numel() != B * H * N * 4:
@@ -321,7 +328,8 @@ def kq_attn_r1_fwd(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: fl
         _dev(q8, torch.uint8, "q8"), _dev(k8, torch.uint8, "k8"), _dev(v8t, torch.uint8, "v8"),
         v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
         float(amax_p), _dev(o, torch.float32, "o"),
-        _dev(row_stats4, torch.float32, "row_stats4"), _stream(stream)), "kq_attn_r1_fwd")
+        _dev(row_stats4, torch.float32, "row_stats4"), _opt(workspace, torch.uint8, "workspace"),
+        0 if workspace is None else workspace.numel(), _stream(stream)), "kq_attn_r1_fwd")
 
 
 def kq_gemm_fp8(a8, b8, s_a: float, s_b: float, c, stream=None):

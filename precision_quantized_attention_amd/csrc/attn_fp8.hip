@@ -228,7 +228,9 @@ __device__ __forceinline__ void mask_tail(v16f (&s)[2], int k0, const Geo& G) {
 // With kFP4 (native MXFP4 BMM1), the 4 MFMAs of BMM1 take the packed E2M1 K rows and their
 // E8M0 scales from LDS and the packed Q operand from registers; they issue in slots 0, 4, 8
 // and 12 of the same 16-slot loop (the P codes of tile j-1 fill every slot).
-template <bool kFP4>
+// With kStats (R1's first pass) there is no P and no BMM2: only BMM1, the row sums and the
+// block maxima, and V is never staged.
+template <bool kFP4, bool kStats>
 __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv)[2], v8i& pop,
                                            int pscale, float d0p, float d1p, v16f (&o)[4],
                                            float& lsum, uint4& kx, uint4& vx, float& mx0,
@@ -270,7 +272,7 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
       const uint8_t* kt = Ks + cur * kKStage + G.kread;
       if (t + 4 < 16) kv[t + 4] = kread(kt, t + 4);
     }
-    if (t >= 8) {
+    if (!kStats && t >= 8) {
       const int c = (t - 8) >> 1, h = (t - 8) & 1;
       vv[t - 8] = *reinterpret_cast<const uint4*>(vt + c * 32 * kVPitch + 16 * h);
     }
@@ -278,10 +280,10 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
       const int blk = t >> 3, i = 2 * (t & 7), w = 4 * blk + (i >> 2);
       const float p0 = pv[blk][i], p1 = pv[blk][i + 1];
       if ((i & 2) == 0) {
-        pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], false);
+        if (!kStats) pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], false);
         pair = p0 + p1;
       } else {
-        pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], true);
+        if (!kStats) pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], true);
         const float q4 = pair + (p0 + p1);
         if (blk) part1 = (i == 2) ? q4 : part1 + q4;
         else part0 = (i == 2) ? q4 : part0 + q4;
@@ -301,7 +303,7 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
   uint2 ka, kb2, kc, kd;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    o[c] = mfma_f8_scaled(cat8(vv[2 * c], vv[2 * c + 1]), pop, o[c], pscale);
+    if (!kStats) o[c] = mfma_f8_scaled(cat8(vv[2 * c], vv[2 * c + 1]), pop, o[c], pscale);
     // block maxima: elements 4c .. 4c + 3 of each block
     if (c == 0) {
       mx0 = fmaxf(fmaxf(sn[0][0], sn[0][1]), fmaxf(sn[0][2], sn[0][3]));
@@ -317,7 +319,7 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
     if constexpr (kFP4) {
       if (c == 2) {
         stage_k<true>(Ks, cur ^ 1, G, kx);
-        stage_v(Vs, cur, G, vx);
+        if (!kStats) stage_v(Vs, cur, G, vx);
       }
     } else {
       if (c == 0) {
@@ -330,13 +332,13 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
         uint8_t* kb = Ks + (cur ^ 1) * kKStage + G.kw;
         *reinterpret_cast<uint4*>(kb) = make_uint4(ka.x, ka.y, kb2.x, kb2.y);
         *reinterpret_cast<uint4*>(kb + 16) = make_uint4(kc.x, kc.y, kd.x, kd.y);
-        stage_v(Vs, cur, G, vx);
+        if (!kStats) stage_v(Vs, cur, G, vx);
       }
     }
     if (c == 3) {
       // past the end the loads return zeros and nothing reads the stages they fill
       kx = kload<kFP4>(G, j + 2);
-      vx = bload16(G.vrs, G.vo + (uint32_t)(j + 1) * kBN);
+      if (!kStats) vx = bload16(G.vrs, G.vo + (uint32_t)(j + 1) * kBN);
     }
     KQ_FENCE();
   }
@@ -575,12 +577,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   if (grp == 1) __syncthreads();
   float mx0, mx1;            // block maxima of the tile just multiplied
   for (int j = 0;; j += 2) {
-    mfma_phase<kFP4>(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
+    mfma_phase<kFP4, kMode == 1>(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
     if (j < ntiles) valu_phase<kMode>(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
     if (j + 1 > ntiles) break;
-    mfma_phase<kFP4>(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
+    mfma_phase<kFP4, kMode == 1>(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
     if (j + 1 < ntiles) valu_phase<kMode>(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
@@ -592,18 +594,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   const float ltot = lsum + __shfl_xor(lsum, 32);      // sum of 448 p relative to m_ref
   const float m_row = fmaxf(m_top, __shfl_xor(m_top, 32));   // the row's M = ceil(max t)
   if (part >= 0) {
-    // partial result of a key range: the unnormalized accumulator and (m_ref, l, M)
+    // partial result of a key range: the unnormalized accumulator and (m_ref, l, M, max raw
+    // score); R1's first pass has no accumulator
     const int row = w * 32 + r;
-    float* wo = a.ws + ((int64_t)part * kBM + row) * kD;
+    if (kMode != 1) {
+      float* wo = a.ws + ((int64_t)part * kBM + row) * kD;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<float4*>(wo + 32 * c + 8 * i4 + 4 * g) =
-            make_float4(o[c][4 * i4], o[c][4 * i4 + 1], o[c][4 * i4 + 2], o[c][4 * i4 + 3]);
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<float4*>(wo + 32 * c + 8 * i4 + 4 * g) =
+              make_float4(o[c][4 * i4], o[c][4 * i4 + 1], o[c][4 * i4 + 2], o[c][4 * i4 + 3]);
+    }
     if (g == 0) {
       float* ws = a.ws + (int64_t)a.rem * a.split * kBM * kD + ((int64_t)part * kBM + row) * 4;
-      *reinterpret_cast<float4*>(ws) = make_float4(m_ref, ltot, m_row, 0.0f);
+      *reinterpret_cast<float4*>(ws) = make_float4(m_ref, ltot, m_row, rmax);
     }
     return;
   }
@@ -637,6 +642,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
 // Merge of the key-range partials of one query block: with R = max m_ref over the parts,
 // acc = sum acc_s 2^(m_ref_s - R) and l = sum l_s 2^(m_ref_s - R) (exact power-of-two scaling),
 // then O = acc * s_v / l as in the single-pass epilogue.  One thread per (row, 4 columns).
+// R1: the second pass's parts share the row's M, and O = acc s_P s_v; the first pass has no
+// accumulator and writes the (M, l, max p) statistics.
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb) {
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int row_all = gid >> 5, d4 = 4 * (gid & 31);
@@ -648,11 +655,12 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
   if (q >= a.n) return;
   const float4* st = reinterpret_cast<const float4*>(a.ws + (int64_t)a.rem * a.split * kBM * kD) +
                      (int64_t)blk * a.split * kBM + row;
-  float R = -INFINITY, m_row = -INFINITY;
+  float R = -INFINITY, m_row = -INFINITY, rmax = -INFINITY;
   for (int s = 0; s < a.split; ++s) {
     const float4 v = st[(int64_t)s * kBM];
     R = fmaxf(R, v.x);
     m_row = fmaxf(m_row, v.z);
+    rmax = fmaxf(rmax, v.w);
   }
   float l = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -660,20 +668,27 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
     const float4 v = st[(int64_t)s * kBM];
     const float f = __builtin_amdgcn_ldexpf(1.0f, (int)(v.x - R));
     l += v.y * f;
-    const float4 x = *reinterpret_cast<const float4*>(
-        a.ws + (((int64_t)blk * a.split + s) * kBM + row) * kD + d4);
-    acc.x += x.x * f;
-    acc.y += x.y * f;
-    acc.z += x.z * f;
-    acc.w += x.w * f;
+    if (a.o != nullptr) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          a.ws + (((int64_t)blk * a.split + s) * kBM + row) * kD + d4);
+      acc.x += x.x * f;
+      acc.y += x.y * f;
+      acc.z += x.z * f;
+      acc.w += x.w * f;
+    }
   }
-  const float scale = a.s_v / l;
-  float* op = a.o + ((int64_t)bh * a.n + q) * kD + d4;
-  *reinterpret_cast<float4*>(op) = make_float4(acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale);
-  if (a.stats != nullptr && d4 == 0) {
-    *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * a.n + q) * 2) =
-        make_float2(m_row, __builtin_amdgcn_ldexpf(l * (1.0f / 448.0f), (int)(R - m_row)));
+  if (a.o != nullptr) {
+    const float scale = a.r1_stats != nullptr ? a.r1_s_p * a.s_v : a.s_v / l;
+    float* op = a.o + ((int64_t)bh * a.n + q) * kD + d4;
+    *reinterpret_cast<float4*>(op) = make_float4(acc.x * scale, acc.y * scale, acc.z * scale, acc.w * scale);
   }
+  if (d4 != 0 || a.r1_stats != nullptr) return;
+  const float lrel = __builtin_amdgcn_ldexpf(l * (1.0f / 448.0f), (int)(R - m_row));
+  if (a.stats != nullptr)
+    *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * a.n + q) * 2) = make_float2(m_row, lrel);
+  if (a.stats4 != nullptr)
+    *reinterpret_cast<float4*>(a.stats4 + ((int64_t)bh * a.n + q) * 4) =
+        make_float4(m_row, lrel, exp2f(rmax * a.c1 - m_row), 0.0f);
 }
 
 // amax_P of R1 from first-pass row statistics: amax[0] = max(amax[0], max over rows of

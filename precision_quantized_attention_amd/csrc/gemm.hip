@@ -56,12 +56,12 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// The scaled MFMA keeps its accumulator in architectural VGPRs, so a wave holds 8 tiles of
-// 32 x 32 (128 registers) and two waves share each SIMD.
+// A wave holds 8 tiles of 32 x 32 (128 accumulator registers) and two waves share each SIMD.
+// FP8 takes the unscaled form (zero scale operands select v_mfma_f32_32x32x64_f8f6f4).
 template <bool kFP4>
 __device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c, int sa, int sb) {
   if (kFP4) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ v8i cat8(uint4 lo, uint4 hi) {
@@ -91,6 +91,18 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][2], const uint8_t* st, int 
     n[i][0] = *reinterpret_cast<const uint4*>(pn);
     n[i][1] = *reinterpret_cast<const uint4*>(pn + 32);
     if (kFP4) sn[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kOpStage + kScStage + sbase_n + i * 32 * 4);
+  }
+  // All operand reads are issued before the first MFMA (the empty asm needs every read's
+  // result): one LDS round trip per step instead of one per sub-tile pair, which the compiler
+  // would otherwise choose to save registers.
+  {
+#define KQ_V4(X_) (u32x4{(X_).x, (X_).y, (X_).z, (X_).w})
+    asm volatile("" ::"v"(KQ_V4(n[0][0])), "v"(KQ_V4(n[0][1])), "v"(KQ_V4(n[1][0])),
+                 "v"(KQ_V4(n[1][1])), "v"(KQ_V4(n[2][0])), "v"(KQ_V4(n[2][1])),
+                 "v"(KQ_V4(n[3][0])), "v"(KQ_V4(n[3][1])), "v"(KQ_V4(m[0][0])),
+                 "v"(KQ_V4(m[0][1])), "v"(KQ_V4(m[1][0])), "v"(KQ_V4(m[1][1])));
+    if (kFP4) asm volatile("" ::"v"(sn[0]), "v"(sn[1]), "v"(sn[2]), "v"(sn[3]), "v"(sm[0]), "v"(sm[1]));
+#undef KQ_V4
   }
   if (kFP4) {
     const uint4 z = make_uint4(0, 0, 0, 0);

@@ -320,12 +320,16 @@ kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
 
 kq_status kq_attn_r1_stats(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                            int v_layout, int B, int H, int N, int d, float s_q, float s_k,
-                           float s_v, float sm_scale, float* row_stats4, hipStream_t stream) {
+                           float s_v, float sm_scale, float* row_stats4, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   kq::AttnParams p;
   // row_stats4 stands in for the output in the shared checks (the first pass writes no O)
   const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
                                    row_stats4, nullptr, &p);
   if (st != KQ_OK) return st;
+  if (!aligned(row_stats4, 16)) return KQ_ERR_INVALID_ARG;
+  const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
+  if (sw != KQ_OK) return sw;
   p.o = nullptr;
   p.stats4 = row_stats4;
   return from_hip(kq::launch_attn_fp8(p, stream));
@@ -341,7 +345,7 @@ kq_status kq_attn_r1_amax(const float* row_stats4, int64_t rows, float* amax_dev
 kq_status kq_attn_r1_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, int v_layout,
                          int B, int H, int N, int d, float s_q, float s_k, float s_v,
                          float sm_scale, float amax_p, float* o_f32, float* row_stats4,
-                         hipStream_t stream) {
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!finite_pos(amax_p) || row_stats4 == nullptr || !aligned(row_stats4, 16))
     return KQ_ERR_INVALID_ARG;
   const float s_p = amax_p / 448.0f, inv_p = 448.0f / amax_p;
@@ -350,6 +354,8 @@ kq_status kq_attn_r1_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8
   const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
                                    o_f32, nullptr, &p);
   if (st != KQ_OK) return st;
+  const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
+  if (sw != KQ_OK) return sw;
   kq::AttnParams p1 = p;
   p1.o = nullptr;
   p1.stats4 = row_stats4;

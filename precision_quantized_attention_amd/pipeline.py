@@ -115,7 +115,7 @@ class QuantizedSDPA:
             b = self.buf
             st = self._r1_stats()
             kq_attn_r1_stats(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
-                             self.scales["v"][0], self.sm_scale, st)
+                             self.scales["v"][0], self.sm_scale, st, self._workspace())
             am = torch.zeros(1, dtype=torch.float32, device=self.device)
             kq_attn_r1_amax(st, am)
             self.amax_p = float(am.item())
@@ -150,17 +150,20 @@ class QuantizedSDPA:
             kq_quantize_fp4_block(v, codes, scales, dq=b.v_dq)
             kq_quantize_fp8_tensor(b.v_dq, self.scales["v"][1], b.v8t, layout=KQ_LAYOUT_TRANSPOSED)
 
-    def attention(self):
-        b = self.buf
+    def _workspace(self):
         if self.workspace is None:
             nbytes = kq_attn_workspace_size(self.B, self.H, self.N, self.d)
             self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=self.device)
                               if nbytes else False)
-        ws = self.workspace if self.workspace is not False else None
+        return self.workspace if self.workspace is not False else None
+
+    def attention(self):
+        b = self.buf
+        ws = self._workspace()
         if self.p_reading == "r1":
             kq_attn_r1_fwd(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
                            self.scales["v"][0], self.sm_scale, self.amax_p, b.o,
-                           self._r1_stats())
+                           self._r1_stats(), ws)
         elif self.native_fp4:
             (qc, qs), (kc, ks) = b.fp4["q"], b.fp4["k"]
             kq_attn_mxfp4_fwd(qc, qs, kc, ks, b.v8t, self.scales["v"][0], self.sm_scale, b.o,

@@ -103,17 +103,23 @@ def test_validation_rejects_before_any_hip_call():
              None) == INVALID
     R1, RS, RA = lib.kq_attn_r1_fwd, lib.kq_attn_r1_stats, lib.kq_attn_r1_amax
     assert R1(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, 0.0, fake, fake,
-              None) == INVALID                                                  # amax_P 0
+              None, 0, None) == INVALID                                         # amax_P 0
     assert R1(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, float("inf"), fake,
-              fake, None) == INVALID
+              fake, None, 0, None) == INVALID
     assert R1(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, 0.5, fake, None,
-              None) == INVALID                                                  # no stats
+              None, 0, None) == INVALID                                         # no stats
     assert R1(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, 0.5, fake, odd,
-              None) == INVALID
+              None, 0, None) == INVALID
     assert R1(fake, fake, fake, 1, 1, 1, 128, 64, 1.0, 1.0, 1.0, 0.1, 0.5, fake, fake,
-              None) == UNSUPPORTED
-    assert RS(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, None, None) == INVALID
-    assert RS(fake, fake, fake, 1, 0, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None) == INVALID
+              None, 0, None) == UNSUPPORTED
+    assert R1(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, 0.5, fake, fake,
+              odd, 1 << 20, None) == INVALID                                    # workspace
+    assert RS(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, None, None, 0,
+              None) == INVALID
+    assert RS(fake, fake, fake, 1, 0, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, 0,
+              None) == INVALID
+    assert RS(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, odd, None, 0,
+              None) == INVALID
     assert RA(None, 4, fake, None) == INVALID
     assert RA(fake, 0, fake, None) == INVALID
     assert RA(odd, 4, fake, None) == INVALID
