@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="override the workload's head count, e.g. 3 = one GPU's share of the "
+                         "Kontext heads under 8-way head sharding")
     ap.add_argument("--native-fp4", action="store_true",
                     help="FP4 workloads: BMM1 on the FP4 Q, K (E2M1 + E8M0) instead of their "
                          "FP8 re-quantization")
@@ -271,6 +274,13 @@ def main():
     c = W.config(args.config)
     torch.cuda.set_device(0)
     q, k, v = (bf16_from_bits(b) for b in W.qkv_bits(args.config))
+    if args.heads is not None:
+        if not 1 <= args.heads <= c.H:
+            print(json.dumps({"error": f"--heads must be in 1..{c.H}"}))
+            sys.exit(2)
+        import dataclasses
+        q, k, v = (x[:, :args.heads].contiguous() for x in (q, k, v))
+        c = dataclasses.replace(c, H=args.heads, name=f"{c.name}_h{args.heads}")
     if args.native_fp4 and c.mode != "fp4":
         print(json.dumps({"error": "--native-fp4 needs an FP4 workload (--config 4 or 5)"}))
         sys.exit(2)
@@ -321,13 +331,34 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     quant_ms = float(np.mean([a.elapsed_time(b) for a, b in quant_ev]))
+    # the same with the 256 MB last-level cache flushed before every call (a 512 MB write), so
+    # the quantizers read their inputs from HBM
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(min(args.steps, 20)):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        m.quantize(q, k, v)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    quant_cold_ms = float(np.median(cold))
 
     flops = c.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    # algorithmic bytes of the quantize step: bf16 in + FP8 out (V transposed) per tensor
+    # algorithmic bytes of the quantize step per element of each tensor: FP8 mode, bf16 in + FP8
+    # out (V transposed); FP4 mode, Q and K bf16 in + codes and scales (+ FP8 unless BMM1 takes
+    # the FP4 form), V bf16 in + codes, scales and bf16 dequant, then the transposed FP8 pass
     n = c.B * c.H * c.N * c.d
-    quant_bytes = 3 * n * 3
+    fp4_out = 0.5 + 1.0 / 32
+    if c.mode == "fp8":
+        quant_bytes = 3 * n * 3
+    else:
+        qk = 2 + fp4_out + (0 if args.native_fp4 else 1)
+        quant_bytes = n * (2 * qk + (2 + fp4_out + 2) + 3)
     out = {
         "metric": "quantized SDPA TFLOP/s @ N=8704,H=24,d=128 + % of MI355X FP8 MFMA peak",
         "value": round(value, 2),
@@ -350,11 +381,14 @@ def main():
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": traffic_bytes() if (args.config == 3 and not args.native_fp4
-                                                    and args.p_reading == "r3") else None},
+                                                    and args.p_reading == "r3"
+                                                    and args.heads is None) else None},
         "pct_fp8_peak_step": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "attention_ms": round(attn_ms, 4),
         "quantize_ms": round(quant_ms, 4),
         "quantize_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quantize_ms_cache_flushed": round(quant_cold_ms, 4),
+        "quantize_gbs_cache_flushed": round(quant_bytes / (quant_cold_ms * 1e-3) / 1e9, 1),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
