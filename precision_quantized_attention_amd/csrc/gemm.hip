@@ -10,8 +10,9 @@
 //   MFMA directly.
 //
 // Work decomposition (CDNA4, wave64): workgroup = 8 waves (two per SIMD) = a 256 x 256 tile of
-// C; wave (wm, wn) computes 64 (m) x 128 (n) = 2 x 4 tiles of 32 x 32 on
-// v_mfma_scale_f32_32x32x64_f8f6f4 (128 accumulator registers).  The product is computed
+// C; wave (wm, wn) computes 64 (m) x 128 (n) = 2 x 4 tiles of 32 x 32 on the 32x32x64 f8f6f4
+// MFMA (the scaled form for MXFP4, the unscaled one for FP8; 128 accumulator registers), with
+// a step's six operand sub-tiles read from LDS before its first MFMA.  The product is computed
 // transposed, D = B_sub · A_sub^T, so each lane owns one row m of C and stores runs of 4
 // consecutive n.  A k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements)
 // through LDS: rows padded to 80 bytes (conflict-free 16-byte operand reads), three stages so
