@@ -156,6 +156,52 @@ def test_attention_key_split_matches_single_pass(B, H, N):
     _compare(np.stack([a2[bb, hh][rows] for bb, hh in hs]), O[0], f"split B{B} H{H} N{N}")
 
 
+def test_attention_beyond_2_31_elements():
+    """4200 heads of N = 4096: Q, K, V hold 2.2e9 elements each (more than 2^31) and O 8.8 GB
+    of float32, so element and byte offsets pass 32 bits in every kernel of the path.  Head h
+    is seeded base head h % 8 rolled by h // 8 rows along the tokens (all heads distinct, the
+    set of values that of the base), so the oracle rebuilds any head from the base."""
+    B, H, N, d, nbase = 1, 4200, 4096, 128, 8
+    assert B * H * N * d > 2 ** 31
+    print(f"large: B={B} H={H} N={N} ({B * H * N * d} elements per tensor)", flush=True)
+    base = [W.random_bits(1, nbase, N, d, seed=1500 + t, outliers=True) for t in range(3)]
+    shifts = torch.arange(H // nbase + 1, device="cuda")
+    tok = torch.arange(N, device="cuda")
+    x = []
+    for b in base:
+        bd = to_dev(b)[0]
+        full = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+        for j in range(nbase):
+            cnt = len(range(j, H, nbase))
+            idx = (tok[None, :] - shifts[:cnt, None]) % N          # np.roll by h // 8 rows
+            full[0, j::nbase] = bd[j][idx]
+        x.append(full)
+        del bd
+    m = QuantizedSDPA(B, H, N, d)
+    m.calibrate(*x)
+    o = m.forward(*x)
+    torch.cuda.synchronize()
+    del x
+    qz = OP.quantize_inputs(*base)
+    for n in "qkv":
+        assert m.amax[n] == qz.amax[n] and m.scales[n] == qz.scale[n], n
+    heads = [0, 2099, 4097, H - 1]                     # 4097 * N * d > 2^31
+    roll = lambda a, h: np.roll(a[0, h % nbase], h // nbase, axis=0)
+    for h in heads:
+        assert np.array_equal(m.buf.q8[0, h].cpu().numpy(), roll(qz.codes["q"], h)), h
+        assert np.array_equal(m.buf.k8[0, h].cpu().numpy(), roll(qz.codes["k"], h)), h
+        assert np.array_equal(m.buf.v8t[h, :, :N].cpu().numpy().T, roll(qz.codes["v"], h)), h
+    rows = sample_rows(N, 8, seed=77)
+    sub = {n: np.stack([roll(qz.codes[n], h) for h in heads])[None] for n in "qkv"}
+    O, _, _ = A.attention_r3(sub["q"], sub["k"], sub["v"], qz.scale["q"][0], qz.scale["k"][0],
+                             qz.scale["v"][0], m.sm_scale, rows=rows)
+    rows_d = torch.from_numpy(rows).cuda()
+    got = np.stack([o[0, h].index_select(0, rows_d).cpu().numpy() for h in heads])
+    _compare(got, O[0], f"H={H} N={N}")
+    del o, m
+    torch.cuda.empty_cache()
+
+
 def test_attention_deterministic():
     bits = [b[:, :4] for b in W.qkv_bits(2)]
     m, o1 = _run(bits)

@@ -220,6 +220,32 @@ def test_gemm_kontext_shapes_sampled(shape, fmt):
     assert torch.isfinite(c).all().item()
 
 
+def test_fp8_gemm_output_beyond_2_31_elements():
+    """M = 262144 tokens (30 Kontext sequences), N = 9216, K = 3072: C holds 2.4e9 float32
+    values (9.7 GB), so output offsets pass 32 bits; sampled rows on both sides of the row
+    where m * N crosses 2^31 and at every tile edge are checked against the exact oracle."""
+    M, N, K = 262144, 9216, 3072
+    assert M * N > 2 ** 31
+    print(f"gemm fp8 large {M}x{N}x{K}", flush=True)
+    rng = np.random.default_rng(2024)
+    a8 = rng.integers(0, 256, size=(M, K), dtype=np.uint8)
+    w8 = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    a8[(a8 & 0x7F) == 0x7F] -= 1                   # no NaN codes
+    w8[(w8 & 0x7F) == 0x7F] -= 1
+    sa, sw = 2.0 ** -6, 2.0 ** -5
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    kq.kq_gemm_fp8(torch.from_numpy(a8).cuda(), torch.from_numpy(w8).cuda(), sa, sw, c)
+    cross = (2 ** 31) // N
+    rows = np.unique(np.concatenate([_sample(M, 7), [cross - 1, cross, cross + 1, cross + 255]]))
+    cols = _sample(N, 8)
+    got = c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    oc = OG.gemm_fp8(a8[rows], w8[cols], sa, sw)
+    L1 = OG.gemm_fp8(a8[rows] & 0x7F, w8[cols] & 0x7F, sa, sw)
+    _check_close(got, oc, L1, K, True, "fp8 large")
+    del c
+    torch.cuda.empty_cache()
+
+
 def test_gemm_overwrites_output_and_is_deterministic():
     """C is fully overwritten (no accumulation into prior contents) and two runs agree bit
     for bit."""
