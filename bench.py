@@ -373,7 +373,8 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": c.name, "B": c.B, "H": c.H, "N": c.N, "d": c.d, "mode": c.mode,
-                   "bmm1": "mxfp4" if args.native_fp4 else "fp8", "p_reading": args.p_reading,
+                   "bmm1": ("mxfp4 codes on the scaled fp4 mfma" if args.native_fp4 else
+                            "e4m3 values on the bf16 mfma"), "p_reading": args.p_reading,
                    "step": ("FP4 quantize Q,K,V (V then FP8) + attention with MXFP4 BMM1"
                             if args.native_fp4 else
                             "quantize Q,K,V to FP8 + fused attention (static scales)")},
