@@ -199,7 +199,8 @@ kq_status kq_attn_r1_stats(const uint8_t* q8, const uint8_t* k8, const uint8_t* 
 
 /* amax_dev[0] = max(amax_dev[0], max over `rows` rows of row_stats4 of fl32(max p / l)): the
  * largest normalized probability.  The caller zero-initializes amax_dev for a fresh
- * calibration; rows = B*H*N. */
+ * calibration; rows = B*H*N.  amax_dev must hold +0 or a positive value: the device takes the
+ * maximum with unsigned atomics on the float bits. */
 kq_status kq_attn_r1_amax(const float* row_stats4, int64_t rows, float* amax_dev,
                           hipStream_t stream);
 

@@ -700,27 +700,33 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
 }
 
 // amax_P of R1 from first-pass row statistics: amax[0] = max(amax[0], max over rows of
-// fl32(pmax / l)), the largest normalized probability.  One workgroup.
-__global__ void __launch_bounds__(1024) r1_amax_kernel(const float* st, int64_t rows, float* amax) {
-  __shared__ float red[1024];
+// fl32(pmax / l)), the largest normalized probability.  Grid-stride over the rows, a
+// workgroup reduction, then one unsigned atomic max on the float bits per workgroup (every
+// value is >= 0, where the unsigned order of the bits is the order of the values).
+__global__ void __launch_bounds__(256) r1_amax_kernel(const float* st, int64_t rows, float* amax) {
+  __shared__ float red[256];
   float m = 0.0f;
-  for (int64_t i = threadIdx.x; i < rows; i += 1024) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows; i += stride) {
     const float4 v = reinterpret_cast<const float4*>(st)[i];
     if (v.y > 0.0f) m = fmaxf(m, v.z / v.y);
   }
   red[threadIdx.x] = m;
   __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
+  for (int w = 128; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
     __syncthreads();
   }
-  if (threadIdx.x == 0) amax[0] = fmaxf(amax[0], red[0]);
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(red[0]));
 }
 
 }  // namespace
 
 hipError_t launch_r1_amax(const float* row_stats4, int64_t rows, float* amax, hipStream_t stream) {
-  hipLaunchKernelGGL(r1_amax_kernel, dim3(1), dim3(1024), 0, stream, row_stats4, rows, amax);
+  // about four rows per thread, at most 512 workgroups (atomics on the one result word)
+  const int64_t g = (rows + 1023) / 1024;
+  const unsigned grid = (unsigned)(g < 1 ? 1 : (g > 512 ? 512 : g));
+  hipLaunchKernelGGL(r1_amax_kernel, dim3(grid), dim3(256), 0, stream, row_stats4, rows, amax);
   return hipGetLastError();
 }
 
