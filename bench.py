@@ -90,6 +90,18 @@ def traffic_bytes():
         return None
 
 
+def host_cpu() -> str:
+    """Model name of the host CPU the oracle baseline runs on (Linux /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, target_s):
     """Time the CPU oracle (as it stands) on a bounded sample of the workload: the full
     per-tensor quantization of Q, K, V, then R3 attention for query rows of successive heads
@@ -217,6 +229,7 @@ def gemm_main(args):
         "gemm_ms": round(kern_ms, 4),
     }
     if not args.no_cpu_baseline:
+        out["host_cpu"] = host_cpu()
         out["cpu_baseline"] = gemm_cpu_baseline(args.gemm, shape, a_bits, w_bits,
                                                 args.cpu_seconds)
     print(json.dumps(out))
@@ -392,6 +405,7 @@ def main():
         "quantize_gbs_cache_flushed": round(quant_bytes / (quant_cold_ms * 1e-3) / 1e9, 1),
     }
     if not args.no_cpu_baseline:
+        out["host_cpu"] = host_cpu()
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(out))
 
