@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--gemm", choices=["fp8", "mxfp4"], default=None,
                     help="time a projection GEMM instead of the attention step")
     ap.add_argument("--gemm-shape", choices=["qkv", "out"], default="qkv")
+    ap.add_argument("--gemm-out", choices=["f32", "bf16"], default="f32",
+                    help="C in float32 (kq_gemm_*) or bf16 (kq_gemm_*_bf16)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="no timing: a plain copy of COPY_BYTES (counter calibration), then 3 "
                          "steps; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
@@ -162,7 +164,8 @@ def gemm_main(args):
     seed = 100 + N
     a_bits, w_bits = W.gemm_bits(M, N, K, seed)
     a, w = bf16_from_bits(a_bits), bf16_from_bits(w_bits)
-    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    bf16_out = args.gemm_out == "bf16"
+    c = torch.empty((M, N), dtype=torch.bfloat16 if bf16_out else torch.float32, device="cuda")
     if args.gemm == "fp8":
         ops = []
         for x in (a, w):
@@ -173,7 +176,8 @@ def gemm_main(args):
             kq.kq_quantize_fp8_tensor(x, inv, y)
             ops.append((y, s_x))
         (a8, sa), (w8, sw) = ops
-        launch = lambda: kq.kq_gemm_fp8(a8, w8, sa, sw, c)
+        gemm = kq.kq_gemm_fp8_bf16 if bf16_out else kq.kq_gemm_fp8
+        launch = lambda: gemm(a8, w8, sa, sw, c)
         peak = FP8_PEAK_TFLOPS
     else:
         ops = []
@@ -184,7 +188,8 @@ def gemm_main(args):
             kq.kq_quantize_fp4_block(x.view(-1, 128), codes.view(-1, 64), scales.view(-1, 4))
             ops.append((codes, scales))
         (ac, asc), (wc, wsc) = ops
-        launch = lambda: kq.kq_gemm_mxfp4(ac, asc, wc, wsc, c)
+        gemm = kq.kq_gemm_mxfp4_bf16 if bf16_out else kq.kq_gemm_mxfp4
+        launch = lambda: gemm(ac, asc, wc, wsc, c)
         peak = FP4_PEAK_TFLOPS
     stream = torch.cuda.current_stream()
     if args.pmc_workload:
@@ -223,7 +228,8 @@ def gemm_main(args):
         "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3" if args.gemm == "fp8" else "mxfp4_e2m1", "data": "synthetic",
         "config": {"workload": shape.name, "M": M, "N": N, "K": K,
-                   "step": "one GEMM launch on prepared codes, float32 C"},
+                   "step": "one GEMM launch on prepared codes, "
+                           + ("bf16 C" if bf16_out else "float32 C")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
         "gemm_ms": round(kern_ms, 4),

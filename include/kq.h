@@ -233,6 +233,16 @@ kq_status kq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                         int64_t K, float* c_f32, hipStream_t stream);
 
+/* The same two products with C delivered in bf16, the activation type of the transformer the
+ * projections sit in: c_bf16 device bf16 [M][N] (16-byte aligned), fully overwritten, each
+ * element the float32 result above rounded once to bf16 (round to nearest even).  Arguments,
+ * sizes and errors as kq_gemm_fp8 / kq_gemm_mxfp4. */
+kq_status kq_gemm_fp8_bf16(const uint8_t* a8, const uint8_t* b8, int64_t M, int64_t N, int64_t K,
+                           float s_a, float s_b, void* c_bf16, hipStream_t stream);
+kq_status kq_gemm_mxfp4_bf16(const uint8_t* a_codes, const uint8_t* a_scales,
+                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                             int64_t N, int64_t K, void* c_bf16, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

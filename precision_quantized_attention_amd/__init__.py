@@ -22,7 +22,7 @@ __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSE
            "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
            "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws",
            "kq_attn_mxfp4_fwd", "kq_attn_r1_stats", "kq_attn_r1_amax", "kq_attn_r1_fwd",
-           "kq_gemm_fp8", "kq_gemm_mxfp4"]
+           "kq_gemm_fp8", "kq_gemm_mxfp4", "kq_gemm_fp8_bf16", "kq_gemm_mxfp4_bf16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_LAYOUT_ROWS = 0
@@ -66,6 +66,8 @@ _SIGNATURES = {
                         ctypes.c_size_t, _P], _I),
     "kq_gemm_fp8": ([_P, _P, _I64, _I64, _I64, _F, _F, _P, _P], _I),
     "kq_gemm_mxfp4": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
+    "kq_gemm_fp8_bf16": ([_P, _P, _I64, _I64, _I64, _F, _F, _P, _P], _I),
+    "kq_gemm_mxfp4_bf16": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
 }
 
 
@@ -332,21 +334,30 @@ def kq_attn_r1_fwd(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: fl
         0 if workspace is None else workspace.numel(), _stream(stream)), "kq_attn_r1_fwd")
 
 
-def kq_gemm_fp8(a8, b8, s_a: float, s_b: float, c, stream=None):
-    """C = s_a s_b E4M3(a8) E4M3(b8)^T.  a8: uint8 [M, K]; b8: uint8 [N, K]; c: float32 [M, N]."""
+def _gemm_fp8(a8, b8, s_a, s_b, c, out_bf16, stream):
     import torch
     M, K = a8.shape
     N = b8.shape[0]
     if b8.dim() != 2 or b8.shape[1] != K or tuple(c.shape) != (M, N):
         raise KQError("expected a8 [M, K], b8 [N, K], c [M, N]")
-    _check(load().kq_gemm_fp8(
+    fn = "kq_gemm_fp8_bf16" if out_bf16 else "kq_gemm_fp8"
+    _check(getattr(load(), fn)(
         _dev(a8, torch.uint8, "a8"), _dev(b8, torch.uint8, "b8"), M, N, K, float(s_a),
-        float(s_b), _dev(c, torch.float32, "c"), _stream(stream)), "kq_gemm_fp8")
+        float(s_b), _dev(c, torch.bfloat16 if out_bf16 else torch.float32, "c"),
+        _stream(stream)), fn)
 
 
-def kq_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, stream=None):
-    """C = dq(a) dq(b)^T from packed E2M1 codes [rows, K/2] and E8M0 scales [rows, K/32];
-    c: float32 [M, N]."""
+def kq_gemm_fp8(a8, b8, s_a: float, s_b: float, c, stream=None):
+    """C = s_a s_b E4M3(a8) E4M3(b8)^T.  a8: uint8 [M, K]; b8: uint8 [N, K]; c: float32 [M, N]."""
+    _gemm_fp8(a8, b8, s_a, s_b, c, False, stream)
+
+
+def kq_gemm_fp8_bf16(a8, b8, s_a: float, s_b: float, c, stream=None):
+    """kq_gemm_fp8 with c bf16 [M, N]: each value the float32 result rounded once (RNE)."""
+    _gemm_fp8(a8, b8, s_a, s_b, c, True, stream)
+
+
+def _gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, out_bf16, stream):
     import torch
     M, Kh = a_codes.shape
     N = b_codes.shape[0]
@@ -354,7 +365,20 @@ def kq_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, stream=None):
     if (b_codes.dim() != 2 or b_codes.shape[1] != Kh or a_scales.numel() != M * (K // 32)
             or b_scales.numel() != N * (K // 32) or tuple(c.shape) != (M, N)):
         raise KQError("expected codes [rows, K/2], scales [rows, K/32], c [M, N]")
-    _check(load().kq_gemm_mxfp4(
+    fn = "kq_gemm_mxfp4_bf16" if out_bf16 else "kq_gemm_mxfp4"
+    _check(getattr(load(), fn)(
         _dev(a_codes, torch.uint8, "a_codes"), _dev(a_scales, torch.uint8, "a_scales"),
         _dev(b_codes, torch.uint8, "b_codes"), _dev(b_scales, torch.uint8, "b_scales"),
-        M, N, K, _dev(c, torch.float32, "c"), _stream(stream)), "kq_gemm_mxfp4")
+        M, N, K, _dev(c, torch.bfloat16 if out_bf16 else torch.float32, "c"),
+        _stream(stream)), fn)
+
+
+def kq_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, stream=None):
+    """C = dq(a) dq(b)^T from packed E2M1 codes [rows, K/2] and E8M0 scales [rows, K/32];
+    c: float32 [M, N]."""
+    _gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, False, stream)
+
+
+def kq_gemm_mxfp4_bf16(a_codes, a_scales, b_codes, b_scales, c, stream=None):
+    """kq_gemm_mxfp4 with c bf16 [M, N]: each value the float32 result rounded once (RNE)."""
+    _gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, True, stream)

@@ -1,6 +1,6 @@
 // Quantized projection GEMMs for gfx950: C = A · B^T with A the activations [M][K] (one row
 // per token) and B the weights [N][K] (one row per output feature), both K-contiguous, C in
-// float32 — the linear layers around the attention in the NVIDIA blog "Optimizing FLUX.1
+// float32 or rounded once to bf16 — the linear layers around the attention in the NVIDIA blog "Optimizing FLUX.1
 // Kontext for Image Editing with Low-Precision Quantization" (section "Workflow and
 // Quantization": per-tensor FP8 and per-block FP4 post-training quantization of the linear
 // layers).
@@ -32,6 +32,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 256;            // workgroup tile of C (M and N)
 constexpr int kThreads = 512;         // 8 waves, two per SIMD
@@ -127,7 +128,13 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][2], const uint8_t* st, int 
   }
 }
 
-template <bool kFP4>
+// Two float32 values -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32) in one dword.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <bool kFP4, bool kBf16>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
   const int tiles_m = (p.m + kTile - 1) / kTile, tiles_n = (p.n + kTile - 1) / kTile;
@@ -233,13 +240,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 #undef KQ_STORE
 
   // epilogue: lane (r, g) owns row m = mt*256 + wm*64 + 32 mi + r and, for each sub-tile ni,
-  // columns n = nt*256 + wn*128 + 32 ni + 8q + 4g .. +3 (q = 0..3)
+  // columns n = nt*256 + wn*128 + 32 ni + 8q + 4g .. +3 (q = 0..3): a float4, or 4 bf16
   const float scale = p.scale;
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
     const int m = mt * kTile + wm * 64 + 32 * mi + r;
     if (m >= p.m) continue;
-    float* crow_p = p.c + (int64_t)m * p.n;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -247,9 +253,14 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
         const int n = nt * kTile + wn * 128 + 32 * ni + 8 * q + 4 * g;
         if (n < p.n) {
           const v16f& c = acc[ni][mi];
-          *reinterpret_cast<float4*>(crow_p + n) =
-              make_float4(c[4 * q] * scale, c[4 * q + 1] * scale, c[4 * q + 2] * scale,
-                          c[4 * q + 3] * scale);
+          const float c0 = c[4 * q] * scale, c1 = c[4 * q + 1] * scale;
+          const float c2 = c[4 * q + 2] * scale, c3 = c[4 * q + 3] * scale;
+          const int64_t off = (int64_t)m * p.n + n;
+          if constexpr (kBf16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + off) =
+                make_uint2(bf16x2_rne(c0, c1), bf16x2_rne(c2, c3));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(p.c) + off) = make_float4(c0, c1, c2, c3);
         }
       }
   }
@@ -259,10 +270,14 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 
 hipError_t launch_gemm(const GemmParams& p, bool fp4, hipStream_t stream) {
   const int tiles = ((p.m + kTile - 1) / kTile) * ((p.n + kTile - 1) / kTile);
-  if (fp4)
-    hipLaunchKernelGGL(gemm_kernel<true>, dim3(tiles), dim3(kThreads), 0, stream, p);
+  if (fp4 && p.out_bf16)
+    hipLaunchKernelGGL((gemm_kernel<true, true>), dim3(tiles), dim3(kThreads), 0, stream, p);
+  else if (fp4)
+    hipLaunchKernelGGL((gemm_kernel<true, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
+  else if (p.out_bf16)
+    hipLaunchKernelGGL((gemm_kernel<false, true>), dim3(tiles), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(gemm_kernel<false>, dim3(tiles), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<false, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -119,7 +119,7 @@ kq_status attn_workspace(int B, int H, int N, void* workspace, size_t workspace_
 // Shared validation of the projection GEMMs: sizes, the K granule of one k-step, N a multiple
 // of 4 (float4 stores of C) and 32-bit buffer offsets for the last tile's prefetches.
 kq_status gemm_params(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, int64_t K,
-                      float* c, int64_t k_granule, int64_t row_bytes, kq::GemmParams* p) {
+                      void* c, int64_t k_granule, int64_t row_bytes, kq::GemmParams* p) {
   if (a == nullptr || b == nullptr || c == nullptr || M < 1 || N < 1 || K < 1)
     return KQ_ERR_INVALID_ARG;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return KQ_ERR_INVALID_ARG;
@@ -134,7 +134,33 @@ kq_status gemm_params(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, 
   p->k = (int)K;
   p->a_scales = p->b_scales = nullptr;
   p->scale = 1.0f;
+  p->out_bf16 = false;
   return KQ_OK;
+}
+
+kq_status gemm_fp8(const uint8_t* a8, const uint8_t* b8, int64_t M, int64_t N, int64_t K,
+                   float s_a, float s_b, void* c, bool out_bf16, hipStream_t stream) {
+  if (!finite_pos(s_a) || !finite_pos(s_b) || !finite_pos(s_a * s_b)) return KQ_ERR_INVALID_ARG;
+  kq::GemmParams p;
+  const kq_status st = gemm_params(a8, b8, M, N, K, c, 64, K, &p);
+  if (st != KQ_OK) return st;
+  p.scale = s_a * s_b;
+  p.out_bf16 = out_bf16;
+  return from_hip(kq::launch_gemm(p, false, stream));
+}
+
+kq_status gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                     const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* c,
+                     bool out_bf16, hipStream_t stream) {
+  if (a_scales == nullptr || b_scales == nullptr) return KQ_ERR_INVALID_ARG;
+  if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return KQ_ERR_INVALID_ARG;
+  kq::GemmParams p;
+  const kq_status st = gemm_params(a_codes, b_codes, M, N, K, c, 128, K / 2, &p);
+  if (st != KQ_OK) return st;
+  p.a_scales = a_scales;
+  p.b_scales = b_scales;
+  p.out_bf16 = out_bf16;
+  return from_hip(kq::launch_gemm(p, true, stream));
 }
 
 }  // namespace
@@ -279,25 +305,24 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
 
 kq_status kq_gemm_fp8(const uint8_t* a8, const uint8_t* b8, int64_t M, int64_t N, int64_t K,
                       float s_a, float s_b, float* c_f32, hipStream_t stream) {
-  if (!finite_pos(s_a) || !finite_pos(s_b) || !finite_pos(s_a * s_b)) return KQ_ERR_INVALID_ARG;
-  kq::GemmParams p;
-  const kq_status st = gemm_params(a8, b8, M, N, K, c_f32, 64, K, &p);
-  if (st != KQ_OK) return st;
-  p.scale = s_a * s_b;
-  return from_hip(kq::launch_gemm(p, false, stream));
+  return gemm_fp8(a8, b8, M, N, K, s_a, s_b, c_f32, false, stream);
+}
+
+kq_status kq_gemm_fp8_bf16(const uint8_t* a8, const uint8_t* b8, int64_t M, int64_t N, int64_t K,
+                           float s_a, float s_b, void* c_bf16, hipStream_t stream) {
+  return gemm_fp8(a8, b8, M, N, K, s_a, s_b, c_bf16, true, stream);
 }
 
 kq_status kq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales,
                         const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
                         int64_t K, float* c_f32, hipStream_t stream) {
-  if (a_scales == nullptr || b_scales == nullptr) return KQ_ERR_INVALID_ARG;
-  if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return KQ_ERR_INVALID_ARG;
-  kq::GemmParams p;
-  const kq_status st = gemm_params(a_codes, b_codes, M, N, K, c_f32, 128, K / 2, &p);
-  if (st != KQ_OK) return st;
-  p.a_scales = a_scales;
-  p.b_scales = b_scales;
-  return from_hip(kq::launch_gemm(p, true, stream));
+  return gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, M, N, K, c_f32, false, stream);
+}
+
+kq_status kq_gemm_mxfp4_bf16(const uint8_t* a_codes, const uint8_t* a_scales,
+                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
+                             int64_t N, int64_t K, void* c_bf16, hipStream_t stream) {
+  return gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, M, N, K, c_bf16, true, stream);
 }
 
 kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,

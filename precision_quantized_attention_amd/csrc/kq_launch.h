@@ -64,9 +64,10 @@ struct GemmParams {
   const uint8_t* b;         // [N][K] / [N][K/2]
   const uint8_t* a_scales;  // [M][K/32] E8M0 (FP4 only)
   const uint8_t* b_scales;  // [N][K/32] E8M0 (FP4 only)
-  float* c;                 // [M][N]
+  void* c;                  // [M][N] float32, or bf16 when out_bf16
   int m, n, k;
   float scale;              // s_a * s_b (FP8), 1 (FP4)
+  bool out_bf16;            // C rounded to bf16 (round to nearest even) instead of float32
 };
 
 // C = A B^T; K % 64 == 0 (FP8) or K % 128 == 0 (FP4), N % 4 == 0.

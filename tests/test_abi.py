@@ -140,6 +140,15 @@ def test_validation_rejects_before_any_hip_call():
     assert G4(fake, fake, fake, ctypes.c_void_p(0x10002), 256, 256, 256, fake, None) == INVALID
     assert G4(fake, fake, fake, fake, 256, 256, 192, fake, None) == UNSUPPORTED  # K % 128
     assert G4(fake, fake, fake, fake, 256, 6, 256, fake, None) == UNSUPPORTED    # N % 4
+    # the bf16-output forms share the validation
+    B8, B4 = lib.kq_gemm_fp8_bf16, lib.kq_gemm_mxfp4_bf16
+    assert B8(fake, fake, 256, 256, 256, 1.0, 1.0, None, None) == INVALID
+    assert B8(fake, fake, 256, 256, 256, 1.0, 1.0, odd, None) == INVALID
+    assert B8(fake, fake, 256, 256, 256, -1.0, 1.0, fake, None) == INVALID
+    assert B8(fake, fake, 256, 256, 96, 1.0, 1.0, fake, None) == UNSUPPORTED   # K % 64
+    assert B8(fake, fake, 256, 258, 256, 1.0, 1.0, fake, None) == UNSUPPORTED  # N % 4
+    assert B4(fake, None, fake, fake, 256, 256, 256, fake, None) == INVALID
+    assert B4(fake, fake, fake, fake, 256, 256, 192, fake, None) == UNSUPPORTED  # K % 128
 
 
 def test_scale_rule_matches_oracle():

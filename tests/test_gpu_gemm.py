@@ -1,4 +1,5 @@
-"""GPU parity of the quantized projection GEMMs (kq_gemm_fp8, kq_gemm_mxfp4) against the oracle.
+"""GPU parity of the quantized projection GEMMs (kq_gemm_fp8, kq_gemm_mxfp4 and their bf16-output
+forms) against the oracle.
 
 Each side quantizes the same seeded bf16 activations and weights with its own code (the HIP
 quantizers on the device, the oracle's on the CPU), the codes must agree bit for bit, and
@@ -19,6 +20,11 @@ run against the full oracle product; the two Kontext projection shapes (M = 8704
 K = 3072, N = 9216 and 3072) are compared on sampled rows and columns, including both ends of
 every tile edge they cross.  Cases whose every product and partial sum is exact in float32
 must match bit for bit.
+
+bf16 output: the float32 result rounded once to nearest even.  Rounding is monotone, so each
+element must lie between the bf16 roundings of (exact - bound) and (exact + bound), equal the
+bf16 rounding of the exact value where the float32 result is exact, and equal torch's bf16
+cast of the float32 entry point's result on the same inputs.
 """
 import numpy as np
 import pytest
@@ -244,6 +250,98 @@ def test_fp8_gemm_output_beyond_2_31_elements():
     _check_close(got, oc, L1, K, True, "fp8 large")
     del c
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ bf16 output
+
+def _bf16_round(x64):
+    """float64 -> bf16 (one round to nearest even) -> float64."""
+    return torch.from_numpy(np.asarray(x64, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _check_bf16(c_bf16, c, L1, K, fp8, what):
+    """The device rounds its float32 result once to bf16, and rounding is monotone, so every
+    element lies between the bf16 roundings of the exact value minus and plus the float32
+    bound."""
+    got = c_bf16.to(torch.float64).cpu().numpy() if isinstance(c_bf16, torch.Tensor) else c_bf16
+    b = _bound(L1, K, fp8)
+    lo, hi = _bf16_round(c - b), _bf16_round(c + b)
+    bad = (got < lo) | (got > hi)
+    assert not bad.any(), (what, np.argwhere(bad)[:3])
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 192), (513, 772, 256), (257, 8, 64)])
+def test_fp8_gemm_bf16_out_matches_oracle(M, N, K):
+    print(f"gemm fp8 bf16-out {M}x{N}x{K}", flush=True)
+    a_bits, w_bits = W.gemm_bits(M, N, K, seed=31 + M + N + K)
+    a8, sa, w8, sw, c32 = _gpu_fp8(a_bits, w_bits)
+    _, _, _, _, oc, L1 = _oracle_fp8(a_bits, w_bits)
+    c16 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kq.kq_gemm_fp8_bf16(a8, w8, sa, sw, c16)
+    torch.cuda.synchronize()
+    _check_bf16(c16, oc, L1, K, True, (M, N, K))
+    # the same kernel's float32 result, rounded by torch: identical bits
+    assert torch.equal(c16, c32.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 256), (513, 772, 256)])
+def test_mxfp4_gemm_bf16_out_matches_oracle(M, N, K):
+    print(f"gemm mxfp4 bf16-out {M}x{N}x{K}", flush=True)
+    a_bits, w_bits = W.gemm_bits(M, N, K, seed=41 + M + N + K)
+    ac, asc, wc, wsc, c32 = _gpu_fp4(a_bits, w_bits)
+    _, _, _, _, oc, L1 = _oracle_fp4(a_bits, w_bits)
+    c16 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kq.kq_gemm_mxfp4_bf16(ac, asc, wc, wsc, c16)
+    torch.cuda.synchronize()
+    _check_bf16(c16, oc, L1, K, False, (M, N, K))
+    assert torch.equal(c16, c32.to(torch.bfloat16))
+
+
+def test_gemm_bf16_out_exact_cases_round_once():
+    """Where every partial sum is exact in float32, the bf16 output is the exact value rounded
+    once to nearest even."""
+    print("gemm bf16-out exact", flush=True)
+    rng = np.random.default_rng(9)
+    M, N, K = 300, 260, 192
+    a8 = rng.choice(_SMALL_E4M3, size=(M, K))
+    w8 = rng.choice(_SMALL_E4M3, size=(N, K))
+    c16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    kq.kq_gemm_fp8_bf16(torch.from_numpy(a8).cuda(), torch.from_numpy(w8).cuda(), 1.0, 3.0, c16)
+    exact = OG.gemm_fp8(a8, w8, 1.0, 3.0)
+    assert np.array_equal(c16.to(torch.float64).cpu().numpy(), _bf16_round(exact))
+    M, N, K = 70, 516, 512
+    ac = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    asc = rng.integers(126, 129, size=(M, K // 32), dtype=np.uint8)
+    wsc = rng.integers(126, 129, size=(N, K // 32), dtype=np.uint8)
+    c16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    kq.kq_gemm_mxfp4_bf16(*[torch.from_numpy(x).cuda() for x in (ac, asc, wc, wsc)], c16)
+    assert np.array_equal(c16.to(torch.float64).cpu().numpy(),
+                          _bf16_round(OG.gemm_mxfp4(ac, asc, wc, wsc)))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_gemm_bf16_out_kontext_qkv_sampled(fmt):
+    shape = W.GEMM_SHAPES[0]
+    M, N, K = shape.M, shape.N, shape.K
+    print(f"gemm {fmt} bf16-out {shape.name}", flush=True)
+    seed = 200 + N
+    a_bits, w_bits = W.gemm_bits(M, N, K, seed)
+    rows, cols = _sample(M, seed), _sample(N, seed + 1)
+    r, q = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    c16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    if fmt == "fp8":
+        a8, sa, w8, sw, _ = _gpu_fp8(a_bits, w_bits)
+        kq.kq_gemm_fp8_bf16(a8, w8, sa, sw, c16)
+        _, _, _, _, oc, L1 = _oracle_fp8(a_bits[rows], w_bits[cols],
+                                         Qz.amax(W.bits_to_f32(a_bits)),
+                                         Qz.amax(W.bits_to_f32(w_bits)))
+    else:
+        ac, asc, wc, wsc, _ = _gpu_fp4(a_bits, w_bits)
+        kq.kq_gemm_mxfp4_bf16(ac, asc, wc, wsc, c16)
+        _, _, _, _, oc, L1 = _oracle_fp4(a_bits[rows], w_bits[cols])
+    _check_bf16(c16[r][:, q], oc, L1, K, fmt == "fp8", (fmt, "bf16", shape.name))
+    assert torch.isfinite(c16.float()).all().item()
 
 
 def test_gemm_overwrites_output_and_is_deterministic():
