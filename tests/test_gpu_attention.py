@@ -202,6 +202,40 @@ def test_attention_beyond_2_31_elements():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("gain", [8.0, 16.0])
+def test_attention_large_score_gaps(gain):
+    """Rows whose scores jump by ~130 (gain 8) or ~260 (gain 16) in the exp2 domain after the
+    first key tiles: the single-pass kernel must move its row reference (the guarded rescale of
+    the accumulators by an exact power of two) and, on the rows where the big keys score far
+    below, clamp block offsets more than 2^126 below the reference; the key split merges parts
+    whose references differ by the same amounts."""
+    print(f"score gaps gain={gain}", flush=True)
+    H, N = 2, 320
+    bits = W.score_gap_bits(H, N, gain, seed=77 + int(gain))
+    m = QuantizedSDPA(1, H, N, 128, want_stats=True)
+    x = [to_dev(b) for b in bits]
+    m.calibrate(*x)
+    m.quantize(*x)
+    qz = OP.quantize_inputs(*bits)
+    _check_codes(m, qz)
+    O, M, _ = OP.attention(qz)
+    assert M[0, :, ::2].min() > 100 and M[0, :, 1::2].max() < 20   # the gaps exist
+    b = m.buf
+    sc = [m.scales[n][0] for n in "qkv"]
+    o1 = torch.empty_like(b.o)
+    st1 = torch.empty_like(b.stats)
+    kq.kq_attn_quant_fwd(b.q8, b.k8, b.v8t, *sc, m.sm_scale, o1, row_stats=st1)
+    nbytes = kq.kq_attn_workspace_size(1, H, N)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(b.o)
+    kq.kq_attn_quant_fwd_ws(b.q8, b.k8, b.v8t, *sc, m.sm_scale, o2, ws)
+    torch.cuda.synchronize()
+    _compare(o1.cpu().numpy(), O, f"gap {gain} single pass")
+    _compare(o2.cpu().numpy(), O, f"gap {gain} key split")
+    st = st1.cpu().numpy()
+    assert np.all(np.abs(st[..., 0] - M) <= 1)
+
+
 def test_attention_deterministic():
     bits = [b[:, :4] for b in W.qkv_bits(2)]
     m, o1 = _run(bits)

@@ -35,7 +35,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "CONFIGS", "config", "qkv_bits", "random_bits", "positions",
-           "bits_to_f32", "GemmShape", "GEMM_SHAPES", "gemm_bits"]
+           "bits_to_f32", "GemmShape", "GEMM_SHAPES", "gemm_bits", "score_gap_bits"]
 
 OUTLIER_FRACTION = 0.01
 OUTLIER_GAIN = 20.0
@@ -115,6 +115,23 @@ def random_bits(B: int, H: int, N: int, d: int, seed: int, outliers: bool = Fals
         for c in _outlier_channels(H, d, seed + 3):
             x[:, c // d, :, c % d] *= np.float32(OUTLIER_GAIN)
     return _to_bf16_bits(x)
+
+
+def score_gap_bits(H: int, N: int, gain: float, seed: int):
+    """(q, k, v) bf16 bits [1, H, N, 128] whose score rows jump by a large power of two after the
+    first key tiles: query rows are +1 (even rows) or -1 (odd rows) in every channel, plus
+    N(0, 0.01^2) noise; keys 0..127 are N(0, 0.01^2), keys 128..191 are `gain` in every
+    channel, the rest N(0, 1); values N(0, 1).  With gain 8 (16) the aligned keys score about
+    130 (261) in the exp2 domain for the +1 rows and as far below for the -1 rows."""
+    assert N > 192
+    g = np.random.Generator(np.random.PCG64(seed))
+    q = np.where((np.arange(N) % 2 == 0)[None, :, None], 1.0, -1.0).astype(np.float32)
+    q = np.broadcast_to(q, (H, N, 128)) + 0.01 * g.standard_normal((H, N, 128), dtype=np.float32)
+    k = g.standard_normal((H, N, 128), dtype=np.float32)
+    k[:, :128] *= np.float32(0.01)
+    k[:, 128:192] = np.float32(gain)
+    v = g.standard_normal((H, N, 128), dtype=np.float32)
+    return tuple(_to_bf16_bits(x[None]) for x in (q, k, v))
 
 
 @functools.lru_cache(maxsize=3)
