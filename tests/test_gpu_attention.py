@@ -218,7 +218,7 @@ def test_attention_large_score_gaps(gain):
     m.quantize(*x)
     qz = OP.quantize_inputs(*bits)
     _check_codes(m, qz)
-    O, M, _ = OP.attention(qz)
+    O, M, L = OP.attention(qz)
     assert M[0, :, ::2].min() > 100 and M[0, :, 1::2].max() < 20   # the gaps exist
     b = m.buf
     sc = [m.scales[n][0] for n in "qkv"]
@@ -234,6 +234,8 @@ def test_attention_large_score_gaps(gain):
     _compare(o2.cpu().numpy(), O, f"gap {gain} key split")
     st = st1.cpu().numpy()
     assert np.all(np.abs(st[..., 0] - M) <= 1)
+    assert np.allclose(st[..., 1].astype(np.float64) * np.exp2(st[..., 0].astype(np.float64) - M),
+                       L.astype(np.float64), rtol=1e-4)
 
 
 def test_attention_deterministic():

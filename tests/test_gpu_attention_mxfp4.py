@@ -122,6 +122,25 @@ def test_mxfp4_attention_every_code_and_scale_spread():
     _compare(o.cpu().numpy(), O, "all codes")
 
 
+@pytest.mark.parametrize("gain", [8.0, 16.0])
+def test_mxfp4_attention_large_score_gaps(gain):
+    """Score rows that jump by ~2^130 / ~2^260 after the first key tiles (the guarded rescale
+    and the offset clamp in the MXFP4-BMM1 instance), single pass and key split."""
+    print(f"mxfp4-bmm1 score gaps gain={gain}", flush=True)
+    bits = W.score_gap_bits(2, 320, gain, seed=77 + int(gain))
+    m, o = _run(bits)
+    qz = OP.quantize_inputs(*bits, mode="fp4")
+    _check_inputs(m, qz)
+    O, M, _ = _oracle(qz, [(0, 0), (0, 1)], np.arange(320), m.sm_scale)
+    assert M[0, :, ::2].min() > 100
+    (qc, qs), (kc, ks) = m.buf.fp4["q"], m.buf.fp4["k"]
+    o1 = torch.empty_like(o)
+    kq.kq_attn_mxfp4_fwd(qc, qs, kc, ks, m.buf.v8t, m.scales["v"][0], m.sm_scale, o1, None)
+    torch.cuda.synchronize()
+    _compare(o1.cpu().numpy()[0], O[0], f"gap {gain} single pass")
+    _compare(o.cpu().numpy()[0], O[0], f"gap {gain} key split")
+
+
 @pytest.mark.parametrize("B,H,N", [(1, 3, 8704), (1, 2, 1000), (1, 2, 65)])
 def test_mxfp4_attention_key_split_matches_single_pass(B, H, N):
     print(f"mxfp4-bmm1 split B={B} H={H} N={N}", flush=True)

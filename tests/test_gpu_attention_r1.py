@@ -155,6 +155,30 @@ def test_r1_kontext_sampled_rows():
     print(f"r1 vs r3 (oracle, same rows): rel_l2 {rel_l2(O[0], O3[0]):.3e}", flush=True)
 
 
+@pytest.mark.parametrize("gain", [8.0, 16.0])
+def test_r1_large_score_gaps(gain):
+    """Score rows that jump by ~2^130 / ~2^260 after the first key tiles: the first pass moves
+    its row reference (guarded rescale) and its statistics must still give the oracle's M, l and
+    amax_P; the second pass then runs at the fixed row offset."""
+    print(f"r1 score gaps gain={gain}", flush=True)
+    bits = W.score_gap_bits(2, 320, gain, seed=77 + int(gain))
+    m = _quantized(bits)
+    _, st, amax_gpu = _r1_gpu(m)
+    qz = OP.quantize_inputs(*bits)
+    args = (qz.codes["q"], qz.codes["k"], qz.codes["v"], qz.scale["q"][0], qz.scale["k"][0],
+            qz.scale["v"][0], m.sm_scale)
+    O, amax_ref = A.attention_r1(*args)
+    assert abs(amax_gpu - amax_ref) <= 1e-5 * amax_ref, (amax_gpu, amax_ref)
+    _, M, L = A.attention_r3(*args)
+    assert M[0, :, ::2].min() > 100
+    assert np.all(np.abs(st[..., 0] - M) <= 1)
+    # l * 2^M compared as l * 2^(M_gpu - M) against the oracle's l (2^M alone overflows)
+    assert np.allclose(st[..., 1].astype(np.float64) * np.exp2(st[..., 0].astype(np.float64) - M),
+                       L.astype(np.float64), rtol=1e-4)
+    o, _, _ = _r1_gpu(m, amax_ref)
+    _compare(o, O, f"r1 gap {gain}", _tie_allowance(*args, amax_ref, np.arange(320)))
+
+
 @pytest.mark.parametrize("H,N", [(3, 8704), (2, 1000), (2, 65)])
 def test_r1_key_split_matches_single_pass(H, N):
     """Both passes through the key split (partials merged by the second kernel) against the
