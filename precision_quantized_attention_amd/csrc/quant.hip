@@ -105,9 +105,10 @@ __global__ void __launch_bounds__(kThreads) fp8_rows_kernel(const uint16_t* __re
 }
 
 // ------------------------------------------------------------------ FP8, transposed layout
-// One workgroup per (batch*head, 64-token tile): read 64 x 128 bf16 rows coalesced, convert,
-// transpose through LDS, write 128 rows of 64 tokens coalesced.  Tokens >= N become 0.
-constexpr int kTT = 64;          // tokens per tile
+// One workgroup per (batch*head, 128-token tile): read 128 x 128 bf16 rows coalesced, convert,
+// transpose through LDS, write 128 rows of 128 tokens coalesced (each row segment a whole
+// 128-byte line, so no line is shared with another workgroup).  Tokens >= N become 0.
+constexpr int kTT = 128;         // tokens per tile (kq_vt_ld pads the rows to a multiple)
 constexpr int kTPad = 4;         // LDS row padding (bytes) against bank conflicts
 
 __global__ void __launch_bounds__(kThreads) fp8_transposed_kernel(const uint16_t* __restrict__ x,
@@ -138,8 +139,8 @@ __global__ void __launch_bounds__(kThreads) fp8_transposed_kernel(const uint16_t
 #pragma unroll
   for (int u = 0; u < (128 * kTT / 16) / kThreads; ++u) {
     const int c = threadIdx.x + u * kThreads;
-    const int d = c >> 2;
-    const int q = c & 3;
+    const int d = c / (kTT / 16);
+    const int q = c % (kTT / 16);
     uint4 v;
     v.x = *reinterpret_cast<const uint32_t*>(&tile[d][16 * q]);
     v.y = *reinterpret_cast<const uint32_t*>(&tile[d][16 * q + 4]);
