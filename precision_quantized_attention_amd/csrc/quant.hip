@@ -51,24 +51,23 @@ __device__ __forceinline__ uint2 e4m3x8(uint4 v, float inv) {
 // max |x| over bf16 magnitudes: for non-NaN values the 15-bit magnitude field orders like
 // |x|, and a non-negative float32 orders like its bit pattern, so the running maximum is an
 // unsigned atomic max on the float bits.
-__global__ void __launch_bounds__(kThreads) amax_bf16_kernel(const uint16_t* __restrict__ x,
-                                                             int64_t n, float* amax) {
+// kT threads per workgroup, kU loads of 16 bytes in flight per thread per step.
+template <int kT, int kU>
+__global__ void __launch_bounds__(kT) amax_bf16_kernel(const uint16_t* __restrict__ x,
+                                                       int64_t n, float* amax) {
   const int64_t n8 = n >> 3;
   const uint4* x8 = reinterpret_cast<const uint4*>(x);
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n8; i += 4 * stride) {
-    uint4 v0 = ld_stream(x8 + i);
-    uint4 v1 = ld_stream(x8 + i + stride);
-    uint4 v2 = ld_stream(x8 + i + 2 * stride);
-    uint4 v3 = ld_stream(x8 + i + 3 * stride);
-    // fold each 32-bit word as two 16-bit magnitudes
+  const int64_t stride = (int64_t)gridDim.x * kT;
+  int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x;
+  // fold each 32-bit word as two 16-bit magnitudes
 #define KQ_FOLD(w) { uint32_t t_ = (w) & 0x7FFF7FFFu; m = max(m, max(t_ & 0xFFFFu, t_ >> 16)); }
-    KQ_FOLD(v0.x) KQ_FOLD(v0.y) KQ_FOLD(v0.z) KQ_FOLD(v0.w)
-    KQ_FOLD(v1.x) KQ_FOLD(v1.y) KQ_FOLD(v1.z) KQ_FOLD(v1.w)
-    KQ_FOLD(v2.x) KQ_FOLD(v2.y) KQ_FOLD(v2.z) KQ_FOLD(v2.w)
-    KQ_FOLD(v3.x) KQ_FOLD(v3.y) KQ_FOLD(v3.z) KQ_FOLD(v3.w)
+  for (; i + (kU - 1) * stride < n8; i += kU * stride) {
+    uint4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = ld_stream(x8 + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) { KQ_FOLD(v[u].x) KQ_FOLD(v[u].y) KQ_FOLD(v[u].z) KQ_FOLD(v[u].w) }
   }
   for (; i < n8; i += stride) {
     uint4 v = ld_stream(x8 + i);
@@ -77,16 +76,16 @@ __global__ void __launch_bounds__(kThreads) amax_bf16_kernel(const uint16_t* __r
 #undef KQ_FOLD
   // tail (n not a multiple of 8): first block only
   if (blockIdx.x == 0) {
-    for (int64_t t = (n8 << 3) + threadIdx.x; t < n; t += kThreads) m = max(m, (uint32_t)(x[t] & 0x7FFFu));
+    for (int64_t t = (n8 << 3) + threadIdx.x; t < n; t += kT) m = max(m, (uint32_t)(x[t] & 0x7FFFu));
   }
   // wave reduction then one atomic per workgroup
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t wmax[kThreads / 64];
+  __shared__ uint32_t wmax[kT / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t b = wmax[0];
-    for (int w = 1; w < kThreads / 64; ++w) b = max(b, wmax[w]);
+    for (int w = 1; w < kT / 64; ++w) b = max(b, wmax[w]);
     atomicMax(reinterpret_cast<unsigned int*>(amax), b << 16);
   }
 }
@@ -243,9 +242,11 @@ int grid_for(int64_t items, int64_t per_block, int cap) {
 }  // namespace
 
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, float* amax, hipStream_t stream) {
-  // 2 workgroups per CU: enough bytes in flight, few atomics on the one result word
-  const int grid = grid_for(n / 8, kThreads * 4, 512);
-  hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, x, n, amax);
+  // at most 256 workgroups of 1024 threads (one per CU), 4 loads of 16 bytes in flight per
+  // thread: enough bytes in flight for HBM, and few atomics on the one result word (the
+  // atomics of many small workgroups serialize on it and cost more than the loads)
+  const int grid = grid_for(n / 8, 1024 * 4, 256);
+  hipLaunchKernelGGL((amax_bf16_kernel<1024, 4>), dim3(grid), dim3(1024), 0, stream, x, n, amax);
   return hipGetLastError();
 }
 
