@@ -43,15 +43,16 @@
 // LDS rows are padded by 16 bytes, which spreads the operand reads of any 8 (or 16)
 // consecutive lanes over distinct 16-byte bank slots.
 //
-// Schedule (measured on gfx950).  A single wave issues a VALU instruction about every 6-7
-// cycles (exp2 and the FP8 conversion cost more) and overlaps only part of that work with its
-// own bf16 MFMAs; when both waves of a SIMD mix MFMA and VALU work finely, the older one takes
-// the matrix pipe and the other stalls behind its MFMA issues.  So the two waves of each SIMD
-// alternate roles (ping-pong): one issues the 20 MFMAs of a tile (matrix-core phase, raised
-// priority) with the light VALU work that fits between them — the E4M3 codes and row sums of
-// the previous tile, the block maxima of this one, the staging — while the other runs the
-// exp2 part of its softmax (VALU phase); workgroup barriers separate the phases.
-// sched_barrier pins the interleaving inside the matrix-core phase.
+// Schedule (measured on gfx950).  A single wave issues an ordinary VALU instruction only
+// about every 8-9 cycles (exp2 and the FP8 conversion about 11), so a tile's softmax costs one
+// wave more cycles than its MFMAs, and the period follows each wave's whole instruction stream.
+// When both waves of a SIMD mix MFMA and VALU work finely, the older one takes the matrix pipe
+// and the other stalls behind its MFMA issues.  So the two waves of each SIMD alternate roles
+// (ping-pong): one issues the 20 MFMAs of a tile (matrix-core phase, raised priority) with the
+// light VALU work that fits between them — the E4M3 codes and row sums of the previous tile,
+// the block maxima of this one, the staging — while the other runs the exp2 part of its
+// softmax (VALU phase); workgroup barriers separate the phases.  sched_barrier pins the
+// interleaving inside the matrix-core phase.
 
 #include "kq_launch.h"
 
