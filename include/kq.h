@@ -134,7 +134,10 @@ kq_status kq_quantize_fp4_block(const void* x_bf16, int64_t rows, int d, uint8_t
  * kq_quantize_fp8_tensor writes it.  s_q, s_k, s_v: per-tensor scales (kq_fp8_scales_from_amax);
  * sm_scale: softmax scale (1/sqrt(128) for these models).
  * o_f32: device float32 [B*H][N][128].  row_stats_or_null: device float32 [B*H][N][2] =
- * (M, sum(p)) per query row, or NULL. */
+ * (M, sum(p)) per query row, or NULL.
+ * Any finite scales: |t| is at most c1 * 448^2 * 128; when that bound reaches 2^20 the kernel
+ * forms each exp2 argument in the definition's order, fl32(raw c1) - M_kb, instead of one
+ * fused multiply-add (slower; only inputs scaled far beyond unit range get there). */
 kq_status kq_attn_quant_fwd(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                             int v_layout, int B, int H, int N, int d, float s_q, float s_k,
                             float s_v, float sm_scale, float* o_f32, float* row_stats_or_null,
@@ -171,7 +174,9 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
  * then softmax, P and BMM2 exactly as kq_attn_quant_fwd (V per-tensor FP8 with scale s_v).
  * q_codes, k_codes: device uint8 [B*H][N][64]; q_scales, k_scales: device uint8 [B*H][N][4]
  * (4-byte aligned); v8, v_layout, o_f32, row_stats_or_null as kq_attn_quant_fwd; workspace as
- * kq_attn_quant_fwd_ws (NULL: no key split; size from kq_attn_workspace_size). */
+ * kq_attn_quant_fwd_ws (NULL: no key split; size from kq_attn_workspace_size).
+ * Precondition: |t| < 2^20, which holds when sm_scale log2(e) 128 max|dq(q)| max|dq(k)| < 2^20
+ * (the E8M0 scales are data, so the library cannot check it; beyond it p may overflow). */
 kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
                             const uint8_t* k_codes, const uint8_t* k_scales, const uint8_t* v8,
                             int v_layout, int B, int H, int N, int d, float s_v, float sm_scale,

@@ -84,6 +84,18 @@ constexpr int kK4Codes = kBN * kK4Pitch;    // 5120 bytes
 constexpr int kK4Stage = kK4Codes + kBN * 4;  // + the 4 scale bytes of every key: 5376 bytes
 constexpr float kLog2_448 = 8.807354922057604f;
 
+// The exp2 argument (t - M_kb + log2 448, t = fl32(raw c1)) is normally one fma,
+// fma(raw, c1, log2 448 - M_kb): exact product, one rounding.  It differs from the definition's
+// order by at most half an ulp of t, so it stays within the rounding of E4M3 (p never passes
+// 464 / 448) while |t| < 2^20, which the host guarantees from the scales (c1 448^2 128 < 2^20)
+// before it launches this form.  Otherwise the kWide instance forms the argument in the
+// definition's order, unfused: fl32(raw c1), minus the offset, plus log2 448.
+__device__ __forceinline__ float unfused_arg(float s, float c1, float m, float add) {
+#pragma clang fp contract(off)
+  const float t = s * c1;
+  return (t - m) + add;
+}
+
 #define KQ_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Buffer resource over `bytes` bytes from `base`: loads past the end return zeros (the
@@ -368,7 +380,7 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
 // and sum l are known from the first pass, so every block uses M, the scale bytes stay 1.0 and
 // the value quantized is p inv_p / l = exp2(t - M + log2(inv_p / l)), saturated at 448.
 // kMode 1 (its first pass) also tracks the row's largest raw score.
-template <int kMode>
+template <int kMode, bool kWide>
 __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float mx1,
                                            float& m_ref, float& m_top, float& lsum,
                                            v16f (&o)[4], int& pscale, float& d0o, float& d1o,
@@ -383,7 +395,9 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
     for (int h = 0; h < 4; ++h) {
       const int kb = h >> 1, i0 = 8 * (h & 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s[kb][i0 + i] = __builtin_fmaf(s[kb][i0 + i], c1, bias);
+      for (int i = 0; i < 8; ++i)
+        s[kb][i0 + i] = kWide ? unfused_arg(s[kb][i0 + i], c1, G.m_fix, G.lb_fix)
+                              : __builtin_fmaf(s[kb][i0 + i], c1, bias);
       KQ_FENCE();
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -428,7 +442,9 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
     const int kb = h >> 1, i0 = 8 * (h & 1);
     const float bias = kb ? bias1 : bias0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s[kb][i0 + i] = __builtin_fmaf(s[kb][i0 + i], c1, bias);
+    for (int i = 0; i < 8; ++i)
+      s[kb][i0 + i] = kWide ? unfused_arg(s[kb][i0 + i], c1, kb ? mb1 : mb0, kLog2_448)
+                            : __builtin_fmaf(s[kb][i0 + i], c1, bias);
     KQ_FENCE();
 #pragma unroll
     for (int i = 0; i < 8; ++i) s[kb][i0 + i] = __builtin_amdgcn_exp2f(s[kb][i0 + i]);
@@ -439,7 +455,7 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
 
 // kMode: 0 the one-pass attention; 1 the same plus the (M, l, max p) row statistics of R1's
 // first pass; 2 R1's second pass.
-template <bool kFP4, int kMode>
+template <bool kFP4, int kMode, bool kWide>
 __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int nqb) {
   constexpr bool kR1 = kMode == 2;
   // bf16 K tiles, or packed E2M1 K tiles + scales (kFP4)
@@ -588,12 +604,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   for (int j = 0;; j += 2) {
     mfma_phase<kFP4, kMode == 1>(j, sA, sB, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
-    if (j < ntiles) valu_phase<kMode>(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
+    if (j < ntiles) valu_phase<kMode, kWide>(j, sA, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
     if (j + 1 > ntiles) break;
     mfma_phase<kFP4, kMode == 1>(j + 1, sB, sA, pop, pscale, d0, d1, o, lsum, kx, vx, mx0, mx1, qop, Ks, Vs, G);
     __syncthreads();
-    if (j + 1 < ntiles) valu_phase<kMode>(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
+    if (j + 1 < ntiles) valu_phase<kMode, kWide>(j + 1, sB, mx0, mx1, m_ref, m_top, lsum, o, pscale, d0, d1, rmax, G);
     __syncthreads();
     if (j + 2 > ntiles) break;
   }
@@ -734,14 +750,21 @@ hipError_t launch_r1_amax(const float* row_stats4, int64_t rows, float* amax, hi
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream) {
   const int nqb = (p.n + kBM - 1) / kBM;
   const int64_t blocks = (int64_t)p.nfull + (int64_t)p.rem * p.split;
-  if (p.r1_stats != nullptr)
-    hipLaunchKernelGGL((attn_fp8_kernel<false, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+  const dim3 g((unsigned)blocks), t(kThreads);
+  if (p.q_scales != nullptr)
+    hipLaunchKernelGGL((attn_fp8_kernel<true, 0, false>), g, t, 0, stream, p, nqb);
+  else if (p.r1_stats != nullptr && p.wide_scores)
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 2, true>), g, t, 0, stream, p, nqb);
+  else if (p.r1_stats != nullptr)
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 2, false>), g, t, 0, stream, p, nqb);
+  else if (p.stats4 != nullptr && p.wide_scores)
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 1, true>), g, t, 0, stream, p, nqb);
   else if (p.stats4 != nullptr)
-    hipLaunchKernelGGL((attn_fp8_kernel<false, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
-  else if (p.q_scales != nullptr)
-    hipLaunchKernelGGL((attn_fp8_kernel<true, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 1, false>), g, t, 0, stream, p, nqb);
+  else if (p.wide_scores)
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 0, true>), g, t, 0, stream, p, nqb);
   else
-    hipLaunchKernelGGL((attn_fp8_kernel<false, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, nqb);
+    hipLaunchKernelGGL((attn_fp8_kernel<false, 0, false>), g, t, 0, stream, p, nqb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split == 0) return e;
   const int64_t cblocks = ((int64_t)p.rem * kBM * 32 + 255) / 256;

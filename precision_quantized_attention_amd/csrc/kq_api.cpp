@@ -86,6 +86,9 @@ kq_status attn_params(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, i
   p->ldv = kq_vt_ld(N);
   p->c1 = (float)c1;
   p->s_v = s_v;
+  // |t| = |raw c1| <= c1 448^2 d over E4M3 codes: past 2^20 the kernel forms the exp2 argument
+  // unfused (see the attention kernel)
+  p->wide_scores = (double)p->c1 * 448.0 * 448.0 * 128.0 >= 1048576.0;
   p->nfull = (int)(bh * nqb);
   p->rem = 0;
   p->split = 0;
@@ -337,6 +340,7 @@ kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
   if (q_scales == nullptr || k_scales == nullptr) return KQ_ERR_INVALID_ARG;
   if (!aligned(q_scales, 4) || !aligned(k_scales, 4)) return KQ_ERR_INVALID_ARG;
   p.q_scales = q_scales;
+  p.wide_scores = false;   // raw carries the E8M0 scales: the documented precondition bounds it
   p.k_scales = k_scales;
   const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
   if (sw != KQ_OK) return sw;

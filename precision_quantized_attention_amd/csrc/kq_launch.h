@@ -33,6 +33,7 @@ struct AttnParams {
   int64_t ldv;
   float c1;               // s_q * s_k * sm_scale * log2(e) (MXFP4: sm_scale * log2(e)), rounded once
   float s_v;
+  bool wide_scores;       // |t| may reach 2^20: the exp2 argument is formed unfused (FP8 only)
   // Key split of the last, partial round of query blocks (split == 0: none).  Query blocks
   // [0, nfull) run whole; each of the `rem` blocks after them runs as `split` workgroups over
   // consecutive key ranges, writing partial results to `ws`, merged by a second kernel.
@@ -40,7 +41,7 @@ struct AttnParams {
   int rem;
   int split;
   float* ws;              // [rem * split][256][128] partial acc, then [rem * split][256][4] stats
-  // Literal FakeQuantize of the normalized P (R1), two passes, no key split.
+  // Literal FakeQuantize of the normalized P (R1), two passes.
   float* stats4;          // first pass: [BH][N][4] = (M, l, max p, 0) per row, or nullptr
   const float* r1_stats;  // second pass: the first pass's stats4 (nullptr: not R1)
   float r1_inv_p;         // 448 / amax_P

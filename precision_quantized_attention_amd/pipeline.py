@@ -22,7 +22,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (KQ_LAYOUT_TRANSPOSED, kq_amax_calibrate, kq_attn_mxfp4_fwd, kq_attn_quant_fwd_ws,
+from . import (KQ_LAYOUT_TRANSPOSED, KQError, kq_amax_calibrate, kq_attn_mxfp4_fwd, kq_attn_quant_fwd_ws,
                kq_attn_r1_amax, kq_attn_r1_fwd, kq_attn_r1_stats,
                kq_attn_workspace_size,
                kq_fp8_scales_from_amax, kq_quantize_fp4_block, kq_quantize_fp8_tensor,
@@ -109,6 +109,12 @@ class QuantizedSDPA:
         a = amax.cpu().numpy()
         self.amax = {n: float(a[i]) for i, n in enumerate("qkv")}
         self.scales = {n: kq_fp8_scales_from_amax(a[i]) for i, n in enumerate("qkv")}
+        if self.native_fp4:
+            # the MXFP4 BMM1 needs |t| < 2^20: |raw| <= 128 max|dq(q)| max|dq(k)|
+            bound = self.sm_scale * math.log2(math.e) * 128.0 * self.amax["q"] * self.amax["k"]
+            if not bound < 2.0 ** 20:
+                raise KQError(f"native MXFP4 BMM1: scores may reach {bound:.3g} in the exp2 "
+                              "domain (limit 2^20); use the FP8 BMM1 (native_fp4=False)")
         if self.p_reading == "r1":
             # amax_P: the largest normalized probability over the calibration inputs
             self.quantize(q, k, v)

@@ -238,6 +238,60 @@ def test_attention_large_score_gaps(gain):
                        L.astype(np.float64), rtol=1e-4)
 
 
+def _scaled_bits(qk_scale, v_scale, seed):
+    return [W.random_bits(1, 2, 300, 128, seed=seed + t, outliers=True,
+                          scale=(v_scale if t == 2 else qk_scale)) for t in range(3)]
+
+
+@pytest.mark.parametrize("qk,vs,sm", [(1e-3, 1e-3, None), (20.0, 1.0, None), (1.0, 1.0, 1.0),
+                                      (1.0, 1.0, 0.02)])
+def test_attention_scale_ranges(qk, vs, sm):
+    """c1 = s_q s_k sm_scale log2 e away from its usual value: all inputs scaled by 1e-3 (the
+    static scales follow the amax), Q and K scaled by 20 (row offsets up to ~11000; the score
+    bound c1 448^2 128 is 25 times 2^20, so the host launches the exp2 argument in the
+    definition's unfused order), and softmax scales 1 (bound 0.71 times 2^20: the fused argument
+    near its limit) and 0.02 (peaked and nearly flat rows)."""
+    print(f"scale ranges qk x{qk} v x{vs} sm={sm}", flush=True)
+    bits = _scaled_bits(qk, vs, 2100)
+    x = [to_dev(b) for b in bits]
+    m = QuantizedSDPA(1, 2, 300, 128, sm_scale=sm, want_stats=True)
+    m.calibrate(*x)
+    o = m.forward(*x)
+    torch.cuda.synchronize()
+    qz = OP.quantize_inputs(*bits)
+    _check_codes(m, qz)
+    O, M, _ = OP.attention(qz, sm_scale=m.sm_scale)
+    print(f"  row offsets M in [{M.min():.0f}, {M.max():.0f}]", flush=True)
+    _compare(o.cpu().numpy(), O, f"qk x{qk} v x{vs} sm={m.sm_scale:.4g}")
+
+
+def test_attention_extreme_score_magnitudes():
+    """Q and K scaled by 1000: scores reach ~1e7 in the exp2 domain, where a float32 ulp is ~1,
+    so the softmax is ill-conditioned (a float32 BMM1 moves single probabilities by factors
+    near 2 against the exact-sum definition) and element-wise parity is not defined there.
+    The kernel must stay finite and form convex combinations of V's rows (up to P's
+    quantization, within 1/16), and agree with the oracle in rel-L2."""
+    print("extreme score magnitudes", flush=True)
+    bits = _scaled_bits(1000.0, 1.0, 2200)
+    x = [to_dev(b) for b in bits]
+    m = QuantizedSDPA(1, 2, 300, 128)
+    m.calibrate(*x)
+    o = m.forward(*x).cpu().numpy().astype(np.float64)
+    qz = OP.quantize_inputs(*bits)
+    O, M, _ = OP.attention(qz)
+    print(f"  row offsets M up to {M.max():.3g}", flush=True)
+    assert np.isfinite(o).all()
+    from oracle import formats as F
+    vd = F.e4m3_decode(qz.codes["v"]) * float(qz.scale["v"][0])         # [1, 2, N, d]
+    lo, hi = vd.min(axis=2, keepdims=True), vd.max(axis=2, keepdims=True)
+    slack = (hi - lo) / 16 + 1e-6
+    assert np.all(o >= lo - slack) and np.all(o <= hi + slack)
+    e = rel_l2(o, O)
+    print(f"  rel_l2 vs oracle {e:.3e}, max_abs {max_abs(o, O):.3e} (|O| max {np.abs(O).max():.3g})",
+          flush=True)
+    assert e <= REL_L2_TOL
+
+
 def test_attention_deterministic():
     bits = [b[:, :4] for b in W.qkv_bits(2)]
     m, o1 = _run(bits)

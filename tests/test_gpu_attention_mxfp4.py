@@ -161,3 +161,17 @@ def test_mxfp4_attention_key_split_matches_single_pass(B, H, N):
         qz = OP.quantize_inputs(*bits, mode="fp4")
         O, _, _ = _oracle(qz, [(0, h) for h in range(H)], np.arange(N), m.sm_scale)
         _compare(b[0], O[0], f"split N={N}")
+
+
+def test_mxfp4_pipeline_refuses_out_of_range_scores():
+    # the MXFP4 BMM1 needs sm_scale log2(e) 128 max|dq(q)| max|dq(k)| < 2^20; inputs scaled by
+    # 1000 exceed it (about 2.6e8), so calibration refuses them instead of launching
+    print("mxfp4-bmm1 range check", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(1400)
+    x = [(torch.randn(1, 2, 256, 128, generator=g) * 1000).to(torch.bfloat16).cuda()
+         for _ in range(3)]
+    m = QuantizedSDPA(1, 2, 256, 128, mode="fp4", native_fp4=True)
+    with pytest.raises(kq.KQError, match="2\\^20"):
+        m.calibrate(*x)
+    m8 = QuantizedSDPA(1, 2, 256, 128, mode="fp4")
+    m8.calibrate(*x)                 # the FP8 BMM1 takes any finite scales
