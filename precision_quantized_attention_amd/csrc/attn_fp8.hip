@@ -656,8 +656,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     if (a.stats != nullptr)
       *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * N + q) * 2) = make_float2(m_row, lrel);
     if (kMode == 1) {
-      // first pass of R1: also the row's largest p = exp2(max t - M)
-      const float pmax = exp2f(rmax * a.c1 - m_row);
+      // first pass of R1: also the row's largest p = exp2(max t - M), its argument formed as
+      // the loop formed those of its p values (fused, or unfused in the kWide instance)
+      const float pmax = exp2f(kWide ? unfused_arg(rmax, a.c1, m_row, 0.0f)
+                                     : __builtin_fmaf(rmax, a.c1, -m_row));
       *reinterpret_cast<float4*>(a.stats4 + ((int64_t)bh * N + q) * 4) =
           make_float4(m_row, lrel, pmax, 0.0f);
     }
@@ -711,9 +713,13 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
   const float lrel = __builtin_amdgcn_ldexpf(l * (1.0f / 448.0f), (int)(R - m_row));
   if (a.stats != nullptr)
     *reinterpret_cast<float2*>(a.stats + ((int64_t)bh * a.n + q) * 2) = make_float2(m_row, lrel);
-  if (a.stats4 != nullptr)
+  if (a.stats4 != nullptr) {
+    // the largest p, its exp2 argument formed as the first pass formed those of its p values
+    const float pmax = exp2f(a.wide_scores ? unfused_arg(rmax, a.c1, m_row, 0.0f)
+                                           : __builtin_fmaf(rmax, a.c1, -m_row));
     *reinterpret_cast<float4*>(a.stats4 + ((int64_t)bh * a.n + q) * 4) =
-        make_float4(m_row, lrel, exp2f(rmax * a.c1 - m_row), 0.0f);
+        make_float4(m_row, lrel, pmax, 0.0f);
+  }
 }
 
 // amax_P of R1 from first-pass row statistics: amax[0] = max(amax[0], max over rows of

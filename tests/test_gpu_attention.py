@@ -263,6 +263,11 @@ def test_attention_scale_ranges(qk, vs, sm):
     O, M, _ = OP.attention(qz, sm_scale=m.sm_scale)
     print(f"  row offsets M in [{M.min():.0f}, {M.max():.0f}]", flush=True)
     _compare(o.cpu().numpy(), O, f"qk x{qk} v x{vs} sm={m.sm_scale:.4g}")
+    b = m.buf                                    # the single pass (no key split) as well
+    o1 = torch.empty_like(b.o)
+    kq.kq_attn_quant_fwd(b.q8, b.k8, b.v8t, *[m.scales[n][0] for n in "qkv"], m.sm_scale, o1)
+    torch.cuda.synchronize()
+    _compare(o1.cpu().numpy(), O, f"qk x{qk} v x{vs} sm={m.sm_scale:.4g} single pass")
 
 
 def test_attention_extreme_score_magnitudes():

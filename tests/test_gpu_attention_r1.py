@@ -219,3 +219,54 @@ def test_r1_key_split_matches_single_pass(H, N):
         allow = _tie_allowance(*args, 0.25, np.arange(N))
         _compare(o0, O, f"r1 unsplit N={N}", allow)
         _compare(o1, O, f"r1 split N={N}", allow)
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_r1_wide_score_range(split):
+    """Q and K scaled by 20 (outlier recipe): the score bound c1 448^2 128 is 25 times 2^20, so
+    both passes form the exp2 argument in the definition's unfused order.  Calibrated amax_P,
+    first-pass statistics and the output against the oracle, single pass and key split."""
+    print(f"r1 wide scores split={split}", flush=True)
+    H, N = 2, 300
+    bits = [W.random_bits(1, H, N, 128, seed=2300 + t, outliers=True,
+                          scale=(1.0 if t == 2 else 20.0)) for t in range(3)]
+    m = _quantized(bits)
+    b = m.buf
+    (sq, _), (sk, _), (sv, _) = m.scales["q"], m.scales["k"], m.scales["v"]
+    c1 = float(sq) * float(sk) * m.sm_scale * np.log2(np.e)
+    assert c1 * 448.0 ** 2 * 128 >= 2.0 ** 20
+    ws = None
+    if split:
+        ws = torch.empty(max(kq.kq_attn_workspace_size(1, H, N), 16), dtype=torch.uint8,
+                         device="cuda")
+    st = torch.empty((1, H, N, 4), dtype=torch.float32, device="cuda")
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    kq.kq_attn_r1_stats(b.q8, b.k8, b.v8t, sq, sk, sv, m.sm_scale, st, ws)
+    kq.kq_attn_r1_amax(st, am)
+    torch.cuda.synchronize()
+    st = st.cpu().numpy()
+    qz = OP.quantize_inputs(*bits)
+    args = (qz.codes["q"], qz.codes["k"], qz.codes["v"], qz.scale["q"][0], qz.scale["k"][0],
+            qz.scale["v"][0], m.sm_scale)
+    O, amax_ref = A.attention_r1(*args)
+    amax_gpu = float(am.item())
+    print(f"amax_P gpu {amax_gpu:.9g} oracle {amax_ref:.9g}", flush=True)
+    assert abs(amax_gpu - amax_ref) <= 1e-5 * amax_ref
+    _, M, L = A.attention_r3(*args)
+    print(f"  row offsets M in [{M.min():.0f}, {M.max():.0f}]", flush=True)
+    assert np.all(np.abs(st[..., 0] - M) <= 1)
+    # the device sums BMM1 in float32, which moves t = fl32(raw c1) by a few units in its last
+    # place; at |t| ~ 1e4 one unit is 2^-10 and scales p by 2^(2^-10): l gets a per-row relative
+    # allowance of 8 such units on top of the 1e-4 of the unit-range tests
+    rtol = 1e-4 + 8 * np.log(2) * np.spacing(np.abs(M).astype(np.float32)).astype(np.float64)
+    lg = st[..., 1].astype(np.float64) * np.exp2(st[..., 0].astype(np.float64) - M)
+    err = np.abs(lg / L.astype(np.float64) - 1)
+    print(f"  l: largest relative difference {err.max():.3e} (allowance {rtol.max():.3e} "
+          f"at the largest M)", flush=True)
+    assert np.all(err <= rtol)
+    o = torch.empty((1, H, N, 128), dtype=torch.float32, device="cuda")
+    kq.kq_attn_r1_fwd(b.q8, b.k8, b.v8t, sq, sk, sv, m.sm_scale, amax_ref, o,
+                      torch.from_numpy(st).cuda(), ws)
+    torch.cuda.synchronize()
+    _compare(o.cpu().numpy(), O, f"r1 wide split={split}",
+             _tie_allowance(*args, amax_ref, np.arange(N)))
