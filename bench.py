@@ -38,7 +38,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~0.1 s of untimed steps: the clock under this load needs about that long to settle
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--config", type=int, default=3, help="workload number (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
