@@ -45,7 +45,8 @@
 //
 // Schedule (measured on gfx950).  A single wave issues an ordinary VALU instruction only
 // about every 8-9 cycles (exp2 and the FP8 conversion about 11), so a tile's softmax costs one
-// wave more cycles than its MFMAs, and the period follows each wave's whole instruction stream.
+// wave more cycles than its MFMAs.  (Under this load the clock settles where the power budget
+// holds it, so the time also follows the energy of the work, mostly the matrix cores'.)
 // When both waves of a SIMD mix MFMA and VALU work finely, the older one takes the matrix pipe
 // and the other stalls behind its MFMA issues.  So the two waves of each SIMD alternate roles
 // (ping-pong): one issues the 20 MFMAs of a tile (matrix-core phase, raised priority) with the
