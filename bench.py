@@ -8,7 +8,7 @@ timed region) followed by the fused attention kernel.
 
 Prints ONE JSON line.  `value` = attention FLOPs (4*B*H*N^2*d) per step / step time, in
 TFLOP/s.  `roofline` describes the attention kernel alone, timed with HIP events on the
-stream it runs on.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
+stream it runs on, around its launch in each timed step.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload (a subset of query rows of a few heads).
 
 `--gemm fp8|mxfp4 --gemm-shape qkv|out` instead times one quantized projection GEMM around the
@@ -206,18 +206,16 @@ def gemm_main(args):
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        launch()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    # timed steps; HIP events on the launch stream bracket each launch inside the timed region
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    t0 = time.perf_counter()
     for e0, e1 in ev:
         e0.record(stream)
         launch()
         e1.record(stream)
     torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
     kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
     value = shape.flops / (ms_per_step * 1e-3) / 1e12
     achieved = shape.flops / (kern_ms * 1e-3) / 1e12
@@ -325,23 +323,19 @@ def main():
         m.forward(q, k, v)
     torch.cuda.synchronize()
 
-    # timed steps
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        m.forward(q, k, v)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
-
-    # attention kernel alone, HIP events around each launch on its stream
+    # timed steps (forward = quantize, then attention); HIP events on the attention's stream
+    # bracket its launch inside each timed step
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
-    m.quantize(q, k, v)
+    t0 = time.perf_counter()
     for a, b in ev:
+        m.quantize(q, k, v)
         a.record(stream)
         m.attention()
         b.record(stream)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     quant_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.steps)]
