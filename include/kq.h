@@ -185,7 +185,7 @@ kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
 
 /* Literal FakeQuantize of the normalized P ("R1"; blog bullet 4 and Fig. 4 read as a
  * FakeQuantize node on the FP32 softmax output with a calibrated per-tensor scale), two
- * passes over the keys, no key split:
+ * passes over the keys (each of them split along the keys when a workspace is given):
  *   pass 1: M = ceil(max t), l = sum exp2(t - M) per row (t as in kq_attn_quant_fwd);
  *   pass 2: P = exp2(t - M) / l, codes = E4M3(P * 448 / amax_P) saturated at 448,
  *           O = (sum codes E4M3(v)) * (amax_P / 448) * s_v.

@@ -16,6 +16,10 @@ ARCH = "gfx950"
 
 SOURCES = ["kq_api.cpp", "quant.hip", "attn_fp8.hip", "gemm.hip"]
 
+# Test-only probe of the matrix instructions' accumulation (tests/probe), built beside libkq.
+PROBE_SRC = os.path.join(ROOT, "tests", "probe", "mfma_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "probe", "libmfma_probe.so")
+
 # Packed FP32 VALU ops stay off: every FP32 instruction is a plain single-lane one.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -56,6 +60,15 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    if os.path.exists(PROBE_SRC):
+        tmp = PROBE_LIB + ".tmp"
+        cmd = [hipcc(), *COMMON, "-shared", PROBE_SRC, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for the probe:\n{r.stderr}")
+        os.replace(tmp, PROBE_LIB)
+        if verbose:
+            print(f"built {PROBE_LIB}")
     return LIB
 
 

@@ -18,14 +18,19 @@
 // pass of the literal FakeQuantize of the normalized P (statistics only); kMode 2, its second
 // pass (the row's M and l known, every block at the same offset).
 //
-// Matrix cores.  BMM1 must accumulate in higher precision (blog bullet 2).  gfx950's FP8
-// MFMA sums its products in groups of 8 along k and truncates every product of a group to
-// 2^-13 of the group's largest one before the float32 accumulate; with the outlier channels
-// of diffusion-transformer activations that shifts scores by ~1e-2 in the exp2 domain.  The
-// bf16 MFMA keeps ~24 bits, and every E4M3 value is exact in bf16, so BMM1 runs on
-// v_mfma_f32_32x32x16_bf16 fed with the E4M3 values of Q and K (converted on chip, the FP8
-// codes stay the interface) — the same products, summed without truncation.  BMM2 keeps the
-// FP8 MFMA (v_mfma_f32_32x32x64_f8f6f4): there the truncation only touches products of tiny
+// Matrix cores.  The page executes QK^T on FP8 (E4M3) inputs (its higher-precision
+// accumulation refers to the projection GEMM that produces Q, K, V); the reading taken here
+// sums BMM1's E4M3 products exactly up to float32 accumulation, as the oracle does.  gfx950's
+// FP8 matrix instructions cannot: every FP8 form (32x32x64 and 16x16x128 f8f6f4, scaled or
+// not, and the older fp8_fp8 forms) adds its products in groups of 8 and truncates each one
+// toward zero to 2^-13 of the group's largest exponent sum (measured on the hardware), which
+// moves scores by ~1e-3 in the exp2 domain; through the E4M3 rounding of P and V's outlier
+// channels that misses the output tolerance (max-abs ~2 on the 512x512 Kontext workload, and
+// still ~0.14 with the 16 largest channels summed exactly).  So, as a departure from running
+// BMM1 on FP8 matrix instructions, BMM1 runs on v_mfma_f32_32x32x16_bf16 fed with the E4M3
+// values of Q and K (each exact in bf16; converted on chip, the FP8 codes stay the interface):
+// the same products, added in float32.  BMM2 keeps the FP8 instruction
+// (v_mfma_scale_f32_32x32x64_f8f6f4): there the truncation only touches products of tiny
 // probabilities, far below the output tolerance.
 //
 // Work decomposition (CDNA4, wave64): workgroup = 8 waves = 256 query rows of one
