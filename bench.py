@@ -31,15 +31,21 @@ sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA peak
 FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 MFMA peak
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
 HBM_PEAK_GBS = 8000.0
+# BMM1 runs on the bf16 matrix instruction (gfx950's FP8 forms truncate the products), BMM2 on
+# the FP8 one: equal FLOPs at 2.5 and 5.0 PFLOP/s bound the attention at their harmonic mean
+MIXED_PEAK_TFLOPS = 2.0 / (1.0 / BF16_PEAK_TFLOPS + 1.0 / FP8_PEAK_TFLOPS)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # ~0.1 s of untimed steps: the clock under this load needs about that long to settle
     ap.add_argument("--warmup", type=int, default=150)
+    # the shader clock under this load takes ~0.1 s of continuous work to settle (and an idle
+    # box starts low), so untimed steps run for this long before the warm-up steps
+    ap.add_argument("--ramp-seconds", type=float, default=0.5)
     ap.add_argument("--config", type=int, default=3, help="workload number (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
@@ -105,49 +111,112 @@ def host_cpu() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, target_s):
+def blas_threads() -> int:
+    """Threads of the BLAS library numpy's matrix products run on (the oracle's products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return 1
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, target_s, gpu_o=None, heads=None):
     """Time the CPU oracle (as it stands) on a bounded sample of the workload: the full
     per-tensor quantization of Q, K, V, then R3 attention for query rows of successive heads
-    until about `target_s` seconds have been spent."""
+    until about `target_s` seconds have been spent.
+
+    With gpu_o (the GPU output [B, H, N, d] of one forward on the same inputs) also returns the
+    GPU's error on the sampled rows: against the oracle (the parity gate's metrics) and against
+    unquantized float64 attention of the bf16 inputs (reported, not gated; its rows are the
+    first 256 of each sampled head, computed after the timing)."""
     import numpy as np
-    import torch
     import workloads as W
     from oracle import attention as A
     from oracle import pipeline as OP
 
     c = W.config(cfg)
+    H = c.H if heads is None else heads
     pos = W.positions(c) if c.rope else None
+    bits = W.qkv_bits(cfg)
+    if heads is not None:
+        bits = tuple(np.ascontiguousarray(b[:, :heads]) for b in bits)
     t0 = time.perf_counter()
-    qz = OP.quantize_inputs(*W.qkv_bits(cfg), mode=c.mode, positions=pos)
+    qz = OP.quantize_inputs(*bits, mode=c.mode, positions=pos)
     t_quant = time.perf_counter() - t0
-    rows_done, heads_done, t_attn = 0, 0, 0.0
+    rows_done, t_attn = 0, 0.0
+    done = []                        # (b, h, rows, O) of the timed sample
     sm = np.float32(1 / math.sqrt(c.d))
     for b in range(c.B):
-        for h in range(c.H):
-            if t_attn + t_quant >= target_s:
+        for h in range(H):
+            if rows_done and t_attn + t_quant >= target_s:
                 break
             sl = (slice(b, b + 1), slice(h, h + 1))
             for r0 in range(0, c.N, 1024):
-                if t_attn + t_quant >= target_s:
+                if rows_done and t_attn + t_quant >= target_s:
                     break
                 rows = np.arange(r0, min(c.N, r0 + 1024))
                 t0 = time.perf_counter()
-                A.attention_r3(qz.codes["q"][sl], qz.codes["k"][sl], qz.codes["v"][sl],
-                               qz.scale["q"][0], qz.scale["k"][0], qz.scale["v"][0], sm,
-                               rows=rows)
+                O, _, _ = A.attention_r3(qz.codes["q"][sl], qz.codes["k"][sl], qz.codes["v"][sl],
+                                         qz.scale["q"][0], qz.scale["k"][0], qz.scale["v"][0], sm,
+                                         rows=rows)
                 t_attn += time.perf_counter() - t0
                 rows_done += len(rows)
-            heads_done += 1
+                done.append((b, h, rows, O[0, 0]))
     # attention FLOPs of the processed rows (4*N*d each) per second; the quantization of the
     # whole tensors is charged in proportion to the rows processed
-    total_rows = c.B * c.H * c.N
+    total_rows = c.B * H * c.N
     flops = 4.0 * rows_done * c.N * c.d
     t = t_attn + t_quant * rows_done / total_rows
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+    heads_done = len({(b, h) for b, h, _, _ in done})
+    base = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": f"{c.name}: FP8 quantization of the full Q, K, V ({t_quant:.1f} s) and R3 "
+            "sample": f"{c.name}: quantization of the full Q, K, V ({t_quant:.1f} s) and R3 "
                       f"attention for {rows_done} query rows in {heads_done} heads "
-                      f"({t_attn:.1f} s); quantization charged pro rata"}
+                      f"({t_attn:.1f} s); quantization charged pro rata; numpy float64 products "
+                      f"on {blas_threads()} BLAS threads of {host_cores()} host cores"}
+    if gpu_o is None:
+        return base, None
+    num = den = 0.0
+    mab = 0.0
+    for b, h, rows, O in done:
+        g = gpu_o[b, h, rows].astype(np.float64)
+        num += float(np.sum((g - O) ** 2))
+        den += float(np.sum(O.astype(np.float64) ** 2))
+        mab = max(mab, float(np.max(np.abs(g - O))))
+    # float64 attention of the unquantized (bf16) inputs, first 256 rows of each sampled head
+    # (after RoPE where the workload has it: the rotation is part of the model, not of the
+    # quantization)
+    fnum = fden = 0.0
+    n64 = 0
+    for b, h in sorted({(b, h) for b, h, _, _ in done}):
+        rows = np.arange(min(256, c.N))
+        xs = [qz.x[n][b:b + 1, h:h + 1] for n in "qkv"]
+        if c.mode == "fp4":        # qz.x holds the FP4-dequantized tensors: start from bf16
+            from oracle import formats as Fm
+            from oracle import rope as R
+            xs = [Fm.bf16_bits_to_f32(x[b:b + 1, h:h + 1]) for x in bits]
+            if pos is not None:
+                tab = R.table(pos)
+                xs[0], xs[1] = R.apply(xs[0], tab), R.apply(xs[1], tab)
+        ref = A.attention_fp64(*xs, float(sm), rows=rows)[0, 0]
+        g = gpu_o[b, h, rows].astype(np.float64)
+        fnum += float(np.sum((g - ref) ** 2))
+        fden += float(np.sum(ref ** 2))
+        n64 += len(rows)
+    parity = {"rows": rows_done, "rel_l2_vs_oracle": math.sqrt(num / den),
+              "max_abs_vs_oracle": mab, "rel_l2_vs_fp64_unquantized": math.sqrt(fnum / fden),
+              "fp64_rows": n64}
+    return base, parity
 
 
 def gemm_main(args):
@@ -271,9 +340,77 @@ def gemm_cpu_baseline(fmt, shape, a_bits, w_bits, target_s):
         rows += len(af)
     flops = 2.0 * rows * shape.N * shape.K
     return {"value": flops / (t + t_w * rows / shape.M) / 1e12, "unit": "TFLOP/s",
-            "cores": torch.get_num_threads(), "kind": "oracle",
+            "cores": blas_threads(), "kind": "oracle",
             "sample": f"{shape.name}: oracle quantization of the weights ({t_w:.1f} s, charged "
-                      f"pro rata) and the exact GEMM of {rows} activation rows ({t:.1f} s)"}
+                      f"pro rata) and the exact GEMM of {rows} activation rows ({t:.1f} s); "
+                      f"numpy float64 products on {blas_threads()} BLAS threads of "
+                      f"{host_cores()} host cores"}
+
+
+def ramp(step, seconds):
+    """Untimed steps for at least `seconds` of wall time (the GPU kept busy throughout), so the
+    timed steps run at the clock this load settles to rather than at the ramp from idle."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n, time.perf_counter() - t0
+
+
+def quantizer_rates(c, q, k, v, m, stream, reps=20):
+    """Each quantizer and calibration kernel of the workload launched alone with the 256 MB
+    last-level cache flushed before every launch (a 512 MB write), timed with HIP events on its
+    stream: microseconds (median) and GB/s of algorithmic bytes (inputs read once, outputs
+    written once).  The FP4 encoder is also timed on the FP8 workloads' Q (codes + scales, and
+    with the fused FP8 output), as the encoder of the FP4 variant on the same tensor size."""
+    import numpy as np
+    import torch
+    import precision_quantized_attention_amd as kq
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    n = q.numel()
+    out = {}
+
+    def timed(name, fn, bytes_per_elem):
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        us = float(np.median(ts))
+        out[name] = {"us": round(us, 2), "gbs": round(n * bytes_per_elem / (us * 1e-6) / 1e9, 1),
+                     "bytes_per_elem": round(bytes_per_elem, 4)}
+
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    timed("amax_bf16", lambda: kq.kq_amax_calibrate(q, am), 2.0)
+    s_q, inv_q = m.scales["q"]
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
+    timed("fp8_rows", lambda: kq.kq_quantize_fp8_tensor(q, inv_q, q8), 3.0)
+    vt = torch.empty_like(m.buf.v8t)
+    timed("fp8_transposed", lambda: kq.kq_quantize_fp8_tensor(
+        v, m.scales["v"][1], vt, layout=kq.KQ_LAYOUT_TRANSPOSED), 3.0)
+    d = q.shape[-1]
+    codes = torch.empty(q.shape[:-1] + (d // 2,), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(q.shape[:-1] + (d // 32,), dtype=torch.uint8, device="cuda")
+    enc = 2 + 0.5 + 1.0 / 32
+    timed("fp4_block", lambda: kq.kq_quantize_fp4_block(q, codes, scales), enc)
+    timed("fp4_block_fp8", lambda: kq.kq_quantize_fp4_block(q, codes, scales, fp8=q8,
+                                                           inv_scale8=inv_q), enc + 1)
+    dq = torch.empty_like(q)
+    timed("fp4_block_dq", lambda: kq.kq_quantize_fp4_block(q, codes, scales, dq=dq), enc + 2)
+    if m.rope is not None:
+        timed("fp4_block_rope_fp8", lambda: kq.kq_quantize_fp4_block(
+            q, codes, scales, fp8=q8, inv_scale8=inv_q, rope=m.rope), enc + 1)
+    del flush
+    return out
 
 
 def main():
@@ -319,6 +456,7 @@ def main():
         print(json.dumps({"pmc_workload": c.name, "copy_bytes": COPY_BYTES, "steps": 3}))
         return
 
+    ramp_steps, ramp_s = ramp(lambda: m.forward(q, k, v), args.ramp_seconds)
     for _ in range(args.warmup):
         m.forward(q, k, v)
     torch.cuda.synchronize()
@@ -337,6 +475,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gpu_o = m.buf.o.cpu().numpy()            # output of the last timed step, for the parity keys
     quant_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.steps)]
     for a, b in quant_ev:
@@ -359,6 +498,7 @@ def main():
         cold.append(a.elapsed_time(b))
     del flush
     quant_cold_ms = float(np.median(cold))
+    kernels = quantizer_rates(c, q, k, v, m, stream)
 
     flops = c.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -373,6 +513,7 @@ def main():
     else:
         qk = 2 + fp4_out + (0 if args.native_fp4 else 1)
         quant_bytes = n * (2 * qk + (2 + fp4_out + 2) + 3)
+    bmm1 = "mxfp4" if args.native_fp4 else "bf16"
     out = {
         "metric": "quantized SDPA TFLOP/s @ N=8704,H=24,d=128 + % of MI355X FP8 MFMA peak",
         "value": round(value, 2),
@@ -398,16 +539,28 @@ def main():
                      "traffic": traffic_bytes() if (args.config == 3 and not args.native_fp4
                                                     and args.p_reading == "r3"
                                                     and args.heads is None) else None},
+        # the same achieved rate against the peak of the instructions the kernel can use: BMM1
+        # on bf16 (FP8 truncates its products), BMM2 on FP8
+        "roofline_mixed_ceiling": ({"peak": round(MIXED_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                                    "frac": round(attn_tflops / MIXED_PEAK_TFLOPS, 4),
+                                    "bmm1": "bf16 2.5 PFLOP/s", "bmm2": "fp8 5.0 PFLOP/s"}
+                                   if bmm1 == "bf16" else None),
         "pct_fp8_peak_step": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "attention_ms": round(attn_ms, 4),
+        "clock_ramp": {"steps": ramp_steps, "seconds": round(ramp_s, 3)},
         "quantize_ms": round(quant_ms, 4),
         "quantize_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "quantize_ms_cache_flushed": round(quant_cold_ms, 4),
         "quantize_gbs_cache_flushed": round(quant_bytes / (quant_cold_ms * 1e-3) / 1e9, 1),
+        "quantizer_kernels_cache_flushed": kernels,
     }
     if not args.no_cpu_baseline:
         out["host_cpu"] = host_cpu()
-        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+        base, parity = cpu_baseline(args.config, args.cpu_seconds, gpu_o=gpu_o, heads=args.heads)
+        out["cpu_baseline"] = base
+        if parity is not None and args.p_reading == "r3" and not args.native_fp4:
+            out["parity_sampled_rows"] = {k_: (round(v_, 8) if isinstance(v_, float) else v_)
+                                          for k_, v_ in parity.items()}
     print(json.dumps(out))
 
 

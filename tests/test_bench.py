@@ -38,15 +38,25 @@ def _check_common(d, steps, warmup):
 @pytest.mark.gpu
 def test_bench_attention_line():
     print("bench: attention line, small workload", flush=True)
-    rc, lines, err = _run("--config", "1", "--steps", "3", "--warmup", "2", "--cpu-seconds", "1")
+    rc, lines, err = _run("--config", "1", "--steps", "3", "--warmup", "2", "--cpu-seconds", "1",
+                          "--ramp-seconds", "0.05")
     assert rc == 0, err[-2000:]
     assert len(lines) == 1
     d = json.loads(lines[0])
     _check_common(d, 3, 2)
     assert d["config"]["N"] == 256 and d["roofline"]["traffic"] is None   # counters: bench shape only
+    mc = d["roofline_mixed_ceiling"]
+    assert mc["peak"] > d["roofline"]["peak"] / 2 and mc["frac"] > d["roofline"]["frac"]
+    assert d["clock_ramp"]["steps"] >= 20
+    for name in ("amax_bf16", "fp8_rows", "fp8_transposed", "fp4_block", "fp4_block_fp8"):
+        kd = d["quantizer_kernels_cache_flushed"][name]
+        assert kd["us"] > 0 and kd["gbs"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert cb["unit"] == "TFLOP/s" and isinstance(cb["sample"], str)
+    par = d["parity_sampled_rows"]
+    assert par["rows"] > 0 and par["rel_l2_vs_oracle"] <= 1e-2 and par["max_abs_vs_oracle"] <= 5e-2
+    assert 0 < par["rel_l2_vs_fp64_unquantized"] < 0.5
 
 
 @pytest.mark.gpu
