@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--gemm-shape", choices=["qkv", "out"], default="qkv")
     ap.add_argument("--gemm-out", choices=["f32", "bf16"], default="f32",
                     help="C in float32 (kq_gemm_*) or bf16 (kq_gemm_*_bf16)")
+    ap.add_argument("--quantizers", action="store_true",
+                    help="only the per-kernel quantizer timing (cache flushed before every "
+                         "launch), one JSON line; the command profiled for the quantizer kernels")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="no timing: a plain copy of COPY_BYTES (counter calibration), then 3 "
                          "steps; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
@@ -454,6 +457,12 @@ def main():
             m.forward(q, k, v)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_workload": c.name, "copy_bytes": COPY_BYTES, "steps": 3}))
+        return
+
+    if args.quantizers:
+        rates = quantizer_rates(c, q, k, v, m, stream, reps=args.steps)
+        print(json.dumps({"quantizer_kernels_cache_flushed": rates, "workload": c.name,
+                          "launches_per_kernel": args.steps, "hbm_peak_gbs": HBM_PEAK_GBS}))
         return
 
     ramp_steps, ramp_s = ramp(lambda: m.forward(q, k, v), args.ramp_seconds)

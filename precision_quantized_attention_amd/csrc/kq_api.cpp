@@ -263,7 +263,7 @@ kq_status kq_quantize_fp4_block(const void* x_bf16, int64_t rows, int d, uint8_t
     if (rope_or_null->cos_sin == nullptr || rope_or_null->n_tokens < 1) return KQ_ERR_INVALID_ARG;
     if (!aligned(rope_or_null->cos_sin, 16)) return KQ_ERR_INVALID_ARG;
     if (rows % rope_or_null->n_tokens != 0) return KQ_ERR_INVALID_ARG;
-    if (d != 128) return KQ_ERR_UNSUPPORTED;
+    if (d != 128 || rows >= ((int64_t)1 << 32)) return KQ_ERR_UNSUPPORTED;
     table = rope_or_null->cos_sin;
     tokens = rope_or_null->n_tokens;
   }
