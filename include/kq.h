@@ -164,6 +164,23 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
                                float* row_stats_or_null, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kq_attn_quant_fwd_ws with the key-split workspace
+ * taken from a static device array of the library instead of the caller.  Same arguments,
+ * rules and results (bit for bit) as kq_attn_quant_fwd_ws given a workspace of
+ * kq_attn_workspace_size bytes.  The array holds 256 x 256 x 132 floats (33 MiB: the partial
+ * results of 256 query blocks' key ranges, every plan of a 256-compute-unit device); a shape
+ * whose plan needs more on the current device is KQ_ERR_UNSUPPORTED.  It allocates nothing:
+ * the array exists once per GPU until the process ends, and its device address is looked up
+ * once per device (hipGetSymbolAddress; a failure is KQ_ERR_HIP).  Every call on a GPU shares
+ * that GPU's array and overwrites what it needs before reading it (nothing has to start at
+ * zero); calls that overlap on one GPU (different streams, or host threads without ordering)
+ * race on it. */
+kq_status kq_attn_quant_fwd_noalloc(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                    int v_layout, int B, int H, int N, int d, float s_q,
+                                    float s_k, float s_v, float sm_scale, float* o_f32,
+                                    float* row_stats_or_null, hipStream_t stream);
+
 /* Attention with a native MXFP4 BMM1 (a hardware-native variant; the blog keeps both
  * products in FP8, so this one is not its numerics): Q and K stay in the per-block FP4 form
  * kq_quantize_fp4_block writes (E2M1 codes + an E8M0 scale per 32 elements of d, RoPE

@@ -21,6 +21,7 @@ __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSE
            "kq_status_string", "kq_vt_ld", "kq_fp8_scales_from_amax", "kq_rope3_table",
            "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
            "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws",
+           "kq_attn_quant_fwd_noalloc",
            "kq_attn_mxfp4_fwd", "kq_attn_r1_stats", "kq_attn_r1_amax", "kq_attn_r1_fwd",
            "kq_gemm_fp8", "kq_gemm_mxfp4", "kq_gemm_fp8_bf16", "kq_gemm_mxfp4_bf16"]
 
@@ -57,6 +58,8 @@ _SIGNATURES = {
     "kq_attn_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)], _I),
     "kq_attn_quant_fwd_ws": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P,
                               ctypes.c_size_t, _P], _I),
+    "kq_attn_quant_fwd_noalloc": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P],
+                                  _I),
     "kq_attn_mxfp4_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P,
                            ctypes.c_size_t, _P], _I),
     "kq_attn_r1_stats": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P,
@@ -252,6 +255,23 @@ def kq_attn_quant_fwd_ws(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_sca
         v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
         _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"), ws, nbytes,
         _stream(stream)), "kq_attn_quant_fwd_ws")
+
+
+def kq_attn_quant_fwd_noalloc(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float,
+                              o, row_stats=None, v_layout: int = KQ_LAYOUT_TRANSPOSED,
+                              stream=None):
+    """kq_attn_quant_fwd_ws with the key-split workspace in the library's static device array
+    (no allocation anywhere: for callers that cannot allocate).  Arguments as
+    kq_attn_quant_fwd; calls that overlap on one GPU race on the shared array."""
+    import torch
+    B, H, N, d = _attn_shapes(q8, k8, v8t, v_layout, o)
+    if row_stats is not None and row_stats.numel() != B * H * N * 2:
+        raise KQError("row_stats must be [B, H, N, 2]")
+    _check(load().kq_attn_quant_fwd_noalloc(
+        _dev(q8, torch.uint8, "q8"), _dev(k8, torch.uint8, "k8"), _dev(v8t, torch.uint8, "v8"),
+        v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
+        _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"),
+        _stream(stream)), "kq_attn_quant_fwd_noalloc")
 
 
 def kq_attn_mxfp4_fwd(q_codes, q_scales, k_codes, k_scales, v8t, s_v: float, sm_scale: float,

@@ -64,6 +64,13 @@
 
 #include <math.h>
 
+#include <mutex>
+
+// Key-split workspace of kq_attn_quant_fwd_noalloc: one copy per GPU, held until the process
+// ends.  Host code never uses this name as an address (it is a host-side stand-in); it uses
+// the device address hipGetSymbolAddress returns, once per device, in attn_static_workspace.
+static __device__ __align__(256) unsigned char scratch[kq::kAttnStaticWorkspaceBytes];
+
 namespace kq {
 namespace {
 
@@ -757,6 +764,25 @@ hipError_t launch_r1_amax(const float* row_stats4, int64_t rows, float* amax, hi
   const unsigned grid = (unsigned)(g < 1 ? 1 : (g > 512 ? 512 : g));
   hipLaunchKernelGGL(r1_amax_kernel, dim3(grid), dim3(256), 0, stream, row_stats4, rows, amax);
   return hipGetLastError();
+}
+
+hipError_t attn_static_workspace(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kAttnStaticWorkspaceBytes;
+  return hipSuccess;
 }
 
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream) {

@@ -306,6 +306,28 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
   return from_hip(kq::launch_attn_fp8(p, stream));
 }
 
+kq_status kq_attn_quant_fwd_noalloc(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                                    int v_layout, int B, int H, int N, int d, float s_q,
+                                    float s_k, float s_v, float sm_scale, float* o_f32,
+                                    float* row_stats_or_null, hipStream_t stream) {
+  kq::AttnParams p;
+  const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
+                                   o_f32, row_stats_or_null, &p);
+  if (st != KQ_OK) return st;
+  const SplitPlan pl = attn_plan(B, H, N);
+  if (pl.split != 0) {
+    void* ws = nullptr;
+    size_t cap = 0;
+    if (kq::attn_static_workspace(&ws, &cap) != hipSuccess) return KQ_ERR_HIP;
+    if (kq::attn_workspace_bytes(pl.rem, pl.split) > cap) return KQ_ERR_UNSUPPORTED;
+    p.nfull = pl.nfull;
+    p.rem = pl.rem;
+    p.split = pl.split;
+    p.ws = static_cast<float*>(ws);
+  }
+  return from_hip(kq::launch_attn_fp8(p, stream));
+}
+
 kq_status kq_gemm_fp8(const uint8_t* a8, const uint8_t* b8, int64_t M, int64_t N, int64_t K,
                       float s_a, float s_b, float* c_f32, hipStream_t stream) {
   return gemm_fp8(a8, b8, M, N, K, s_a, s_b, c_f32, false, stream);

@@ -52,11 +52,19 @@ struct AttnParams {
 constexpr int kAttnRowsPerBlock = 256;
 
 // Bytes of workspace for `rem * split` partial query blocks.
-inline size_t attn_workspace_bytes(int rem, int split) {
+constexpr size_t attn_workspace_bytes(int rem, int split) {
   return (size_t)rem * split * kAttnRowsPerBlock * (128 + 4) * sizeof(float);
 }
 
 hipError_t launch_attn_fp8(const AttnParams& p, hipStream_t stream);
+
+// The static key-split workspace: partial results of up to 256 query blocks' key ranges, the
+// most a 256-compute-unit device's plan uses (rem * split <= compute units).
+constexpr size_t kAttnStaticWorkspaceBytes = attn_workspace_bytes(1, 256);
+
+// Device address and size of the static workspace on the current device (looked up once per
+// device with hipGetSymbolAddress).
+hipError_t attn_static_workspace(void** ptr, size_t* bytes);
 
 hipError_t launch_r1_amax(const float* row_stats4, int64_t rows, float* amax, hipStream_t stream);
 

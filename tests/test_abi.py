@@ -82,6 +82,12 @@ def test_validation_rejects_before_any_hip_call():
              None) == UNSUPPORTED
     assert W(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, odd, 1 << 20,
              None) == INVALID
+    Z = lib.kq_attn_quant_fwd_noalloc            # the attention checks, before any HIP call
+    assert Z(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, None, None, None) == INVALID
+    assert Z(fake, fake, fake, 1, 1, 1, 128, 64, 1.0, 1.0, 1.0, 0.1, fake, None, None) == UNSUPPORTED
+    assert Z(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, float("nan"), 0.1, fake, None,
+             None) == INVALID
+    assert Z(odd, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, None) == INVALID
     n = ctypes.c_size_t(0)
     S = lib.kq_attn_workspace_size
     assert S(1, 1, 128, 128, None) == INVALID
