@@ -25,4 +25,5 @@ Modules:
   attention  R3 quantized attention (gated), R1 variant and FP64 reference (reported)
   pipeline   the whole path for one workload: RoPE -> FP4 -> calibrate -> FP8 -> attention
   gemm       quantized projection GEMMs (per-tensor FP8 W8A8, per-block MXFP4), exact float64
+  svdquant   SVD-Quant in FP4 of a projection GEMM: rank-r bf16 branch + MXFP4 residual
 """

@@ -35,7 +35,8 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "CONFIGS", "config", "qkv_bits", "random_bits", "positions",
-           "bits_to_f32", "GemmShape", "GEMM_SHAPES", "gemm_bits", "score_gap_bits"]
+           "bits_to_f32", "GemmShape", "GEMM_SHAPES", "gemm_bits", "score_gap_bits",
+           "lowrank_weight_bits", "PLANTED_RANK"]
 
 OUTLIER_FRACTION = 0.01
 OUTLIER_GAIN = 20.0
@@ -177,6 +178,28 @@ GEMM_SHAPES = [
     GemmShape("kontext_1024_qkv_proj", 8704, 3 * 3072, 3072),
     GemmShape("kontext_1024_out_proj", 8704, 3072, 3072),
 ]
+
+
+PLANTED_RANK = 8
+
+
+def lowrank_weight_bits(N: int, K: int, seed: int, planted_rank: int = PLANTED_RANK,
+                        gain: float = 8.0, cols=None):
+    """bf16 bits of weights [N, K] with a planted low-rank outlier component, the structure the
+    SVD-Quant branch is meant to absorb: N(0, 1/K) entries (seed) plus `planted_rank` rank-one
+    terms g_i u_i v_i^T / sqrt(K), u_i ~ N(0, 1)^N, v_i ~ N(0, 1)^K (seed + 1, seed + 2), with
+    g_i = gain * 2^(-i/2).  Each planted term's entries are ~g_i times the base spread.  `cols`
+    (index array or None) selects output rows (weight rows) without changing their values."""
+    w = _draw((N, K), seed) * np.float32(1.0 / np.sqrt(K))
+    g1 = np.random.Generator(np.random.PCG64(seed + 1))
+    g2 = np.random.Generator(np.random.PCG64(seed + 2))
+    u = g1.standard_normal((N, planted_rank), dtype=np.float32)
+    v = g2.standard_normal((planted_rank, K), dtype=np.float32)
+    gains = (gain * 2.0 ** (-0.5 * np.arange(planted_rank)) / np.sqrt(K)).astype(np.float32)
+    w = w + (u * gains) @ v
+    if cols is not None:
+        w = w[np.asarray(cols)]
+    return _to_bf16_bits(w.astype(np.float32))
 
 
 def gemm_bits(M: int, N: int, K: int, seed: int, rows=None, cols=None):
