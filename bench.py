@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--gemm", choices=["fp8", "mxfp4"], default=None,
                     help="time a projection GEMM instead of the attention step")
     ap.add_argument("--gemm-shape", choices=["qkv", "out"], default="qkv")
+    ap.add_argument("--svdquant-rank", type=int, default=0,
+                    help="with --gemm mxfp4: SVD-Quant in FP4, a rank-r bf16 branch plus the "
+                         "MXFP4 GEMM of the residual (weights with a planted low-rank part)")
     ap.add_argument("--gemm-out", choices=["f32", "bf16"], default="f32",
                     help="C in float32 (kq_gemm_*) or bf16 (kq_gemm_*_bf16)")
     ap.add_argument("--quantizers", action="store_true",
@@ -224,7 +227,10 @@ def cpu_baseline(cfg, target_s, gpu_o=None, heads=None):
 
 def gemm_main(args):
     """One JSON line for a projection GEMM: a step is one kq_gemm_* launch on codes prepared
-    (quantized by the library's own kernels) before the timed region."""
+    (quantized by the library's own kernels) before the timed region.  With --svdquant-rank r
+    (MXFP4 only) the weights carry a planted low-rank part, the library's offline step splits
+    them into bf16 rank-r factors and a residual (untimed), and a step is the branch's
+    down-projection plus the fused GEMM."""
     import numpy as np
     import torch
     import workloads as W
@@ -233,12 +239,25 @@ def gemm_main(args):
 
     shape = W.GEMM_SHAPES[0 if args.gemm_shape == "qkv" else 1]
     M, N, K = shape.M, shape.N, shape.K
+    rank = args.svdquant_rank
+    if rank and args.gemm != "mxfp4":
+        print(json.dumps({"error": "--svdquant-rank needs --gemm mxfp4"}))
+        sys.exit(2)
     torch.cuda.set_device(0)
     seed = 100 + N
     a_bits, w_bits = W.gemm_bits(M, N, K, seed)
-    a, w = bf16_from_bits(a_bits), bf16_from_bits(w_bits)
+    t_prep = 0.0
+    if rank:
+        w_bits = W.lowrank_weight_bits(N, K, seed + 7)
+        t0 = time.perf_counter()
+        lu_bits, ld_bits, r_bits = kq.kq_svdquant_factorize(w_bits, rank)   # offline, host
+        t_prep = time.perf_counter() - t0
+        l_up, l_down = bf16_from_bits(lu_bits), bf16_from_bits(ld_bits)
+    a, w = bf16_from_bits(a_bits), bf16_from_bits(r_bits if rank else w_bits)
     bf16_out = args.gemm_out == "bf16"
     c = torch.empty((M, N), dtype=torch.bfloat16 if bf16_out else torch.float32, device="cuda")
+    flops = shape.flops + (2 * M * rank * (K + N) if rank else 0)
+    down = None
     if args.gemm == "fp8":
         ops = []
         for x in (a, w):
@@ -261,66 +280,119 @@ def gemm_main(args):
             kq.kq_quantize_fp4_block(x.view(-1, 128), codes.view(-1, 64), scales.view(-1, 4))
             ops.append((codes, scales))
         (ac, asc), (wc, wsc) = ops
-        gemm = kq.kq_gemm_mxfp4_bf16 if bf16_out else kq.kq_gemm_mxfp4
-        launch = lambda: gemm(ac, asc, wc, wsc, c)
+        if rank:
+            # per forward: one pass over the activations (their MXFP4 codes and the branch's
+            # T), then the fused GEMM
+            t = torch.empty((M, rank), dtype=torch.bfloat16, device="cuda")
+            gemm = kq.kq_gemm_mxfp4_svdquant_bf16 if bf16_out else kq.kq_gemm_mxfp4_svdquant
+            down = lambda: kq.kq_svdquant_activations(a, l_down, ac, asc, t)
+            launch = lambda: gemm(ac, asc, wc, wsc, t, l_up, c)
+        else:
+            gemm = kq.kq_gemm_mxfp4_bf16 if bf16_out else kq.kq_gemm_mxfp4
+            launch = lambda: gemm(ac, asc, wc, wsc, c)
         peak = FP4_PEAK_TFLOPS
     stream = torch.cuda.current_stream()
+
+    def step():
+        if down is not None:
+            down()
+        launch()
+
     if args.pmc_workload:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         for _ in range(3):
-            launch()
+            step()
         torch.cuda.synchronize()
         print(json.dumps({"pmc_workload": shape.name, "copy_bytes": COPY_BYTES, "steps": 3}))
         return
+    ramp(step, args.ramp_seconds)
     for _ in range(args.warmup):
-        launch()
+        step()
     torch.cuda.synchronize()
-    # timed steps; HIP events on the launch stream bracket each launch inside the timed region
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # timed steps; HIP events on the launch stream bracket the GEMM launch (and the branch's
+    # down-projection) inside the timed region
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for e0, e1 in ev:
+    for e0, e1, e2 in ev:
         e0.record(stream)
-        launch()
+        if down is not None:
+            down()
         e1.record(stream)
+        launch()
+        e2.record(stream)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
-    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
-    value = shape.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = shape.flops / (kern_ms * 1e-3) / 1e12
-    fmt_name = "FP8 E4M3 per-tensor (W8A8)" if args.gemm == "fp8" else "MXFP4 (E2M1, E8M0 per 32)"
+    kern_ms = float(np.mean([e1.elapsed_time(e2) for e0, e1, e2 in ev]))
+    down_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, e2 in ev])) if rank else 0.0
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = (flops - (2 * M * rank * K if rank else 0)) / (kern_ms * 1e-3) / 1e12
+    if rank:
+        fmt_name = f"SVD-Quant FP4: MXFP4 residual + rank-{rank} bf16 branch"
+    else:
+        fmt_name = "FP8 E4M3 per-tensor (W8A8)" if args.gemm == "fp8" else "MXFP4 (E2M1, E8M0 per 32)"
     out = {
         "metric": f"quantized projection GEMM TFLOP/s ({fmt_name})",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3" if args.gemm == "fp8" else "mxfp4_e2m1", "data": "synthetic",
-        "config": {"workload": shape.name, "M": M, "N": N, "K": K,
-                   "step": "one GEMM launch on prepared codes, "
+        "config": {"workload": shape.name + (f"_svdquant_r{rank}" if rank else ""), "M": M,
+                   "N": N, "K": K, "rank": rank,
+                   "step": ("activation pass (MXFP4 codes of A + branch down-projection) + fused "
+                            "GEMM (MXFP4 residual + branch), " if rank
+                            else "one GEMM launch on prepared codes, ")
                            + ("bf16 C" if bf16_out else "float32 C")},
+        # the GEMM launch alone: its MXFP4 FLOPs plus the branch's up-projection, at the FP4 peak
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
         "gemm_ms": round(kern_ms, 4),
     }
+    if rank:
+        # the activation pass: A read once, its codes and scales and T written
+        out["svdquant_activations_ms"] = round(down_ms, 4)
+        out["svdquant_activations_gbs"] = round(
+            M * (K * (2 + 0.5 + 1.0 / 32) + 2 * rank) / (down_ms * 1e-3) / 1e9, 1)
+        out["svdquant_factorize_host_s"] = round(t_prep, 2)
     if not args.no_cpu_baseline:
         out["host_cpu"] = host_cpu()
         out["cpu_baseline"] = gemm_cpu_baseline(args.gemm, shape, a_bits, w_bits,
-                                                args.cpu_seconds)
+                                                args.cpu_seconds, rank=rank)
     print(json.dumps(out))
 
 
-def gemm_cpu_baseline(fmt, shape, a_bits, w_bits, target_s):
+def gemm_cpu_baseline(fmt, shape, a_bits, w_bits, target_s, rank=0):
     """The oracle GEMM (exact float64) on successive 64-row blocks of the activations against
-    all weights, quantized by the oracle, until about `target_s` seconds."""
+    all weights, quantized by the oracle, until about `target_s` seconds.  SVD-Quant: the
+    oracle's offline weight step (float64 SVD, not charged: it is not part of the forward),
+    then its forward on successive 64-row blocks."""
     import numpy as np
-    import torch
     import workloads as W
     from oracle import gemm as OG
     from oracle import quant as Qz
 
+    if rank:
+        from oracle import svdquant as OS
+        t0 = time.perf_counter()
+        prep = OS.quantize_weights(W.bits_to_f32(w_bits), rank)
+        t_off = time.perf_counter() - t0
+        rows, t = 0, 0.0
+        while (t < target_s or rows == 0) and rows < shape.M:
+            af = W.bits_to_f32(a_bits[rows:rows + 64])
+            t0 = time.perf_counter()
+            OS.forward(af, prep[0], prep[1], prep[3], prep[4])
+            t += time.perf_counter() - t0
+            rows += len(af)
+        flops = 2.0 * rows * (shape.N * shape.K + rank * (shape.K + shape.N))
+        return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                "kind": "oracle",
+                "sample": f"{shape.name} SVD-Quant r={rank}: oracle forward (FP4 quantization "
+                          f"of the rows, exact GEMM, bf16 branch) of {rows} activation rows "
+                          f"({t:.1f} s); the offline weight step ({t_off:.1f} s) not charged; "
+                          f"numpy float64 products on {blas_threads()} BLAS threads of "
+                          f"{host_cores()} host cores"}
     t0 = time.perf_counter()
     wf = W.bits_to_f32(w_bits)
     if fmt == "fp8":

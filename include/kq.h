@@ -164,6 +164,53 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
                                float* row_stats_or_null, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* SVD-Quant in FP4 for a projection GEMM (blog section "Workflow and Quantization", which names
+ * SVD-Quant in FP4 beside PTQ in FP8 and FP4; the page gives none of its steps, so this is the
+ * method's plainest form).  Offline, the bf16 weights W [N][K] are split into rank-r bf16
+ * factors L_up [N][r], L_down [r][K] (from W's SVD) and the bf16 residual
+ * R = W - L_up L_down, whose MXFP4 codes and scales come from kq_quantize_fp4_block like any
+ * weight's.  Per forward:
+ *   kq_svdquant_down:        T = bf16(A L_down^T), A [M][K] bf16 activations, T [M][r] bf16
+ *                            (each value the float32 sum rounded once, nearest even);
+ *   kq_gemm_mxfp4_svdquant:  C = dq(A4) dq(R4)^T + T L_up^T, float32 accumulation, C float32
+ *                            [M][N] (the _bf16 form rounds C once to bf16, nearest even);
+ *                            A4, R4 as kq_gemm_mxfp4's operands.
+ * Device pointers, 16-byte aligned (scales 4-byte).  r % 16 == 0 with r <= 64 (down) and
+ * r <= 256 (GEMM), K % 64 == 0 (down) and K % 128 == 0 (GEMM); otherwise KQ_ERR_UNSUPPORTED,
+ * as are sizes whose byte offsets pass 2^31.  Other rules as kq_gemm_mxfp4. */
+kq_status kq_svdquant_down(const void* a_bf16, const void* l_down_bf16, int64_t M, int64_t K,
+                           int rank, void* t_bf16, hipStream_t stream);
+/* The activation pass of a forward in one read of A: kq_svdquant_down's T, and A's MXFP4 codes
+ * [M][K/2] and E8M0 scales [M][K/32], equal bit for bit to kq_quantize_fp4_block's on A
+ * (a_codes 16-byte aligned).  Same rules as kq_svdquant_down. */
+kq_status kq_svdquant_activations(const void* a_bf16, const void* l_down_bf16, int64_t M,
+                                  int64_t K, int rank, uint8_t* a_codes, uint8_t* a_scales,
+                                  void* t_bf16, hipStream_t stream);
+
+/* The offline weight step (host only; no HIP call): from the bf16 weights w [N][K] (host
+ * memory), the rank-r bf16 factors l_up [N][r] = U_r S_r and l_down [r][K] = V_r^T of W's
+ * leading singular triplets, and the bf16 residual [N][K] = W - l_up l_down (with the rounded
+ * factors), every value rounded once to nearest even.  The triplets come from a randomized
+ * range finder (fixed seed, r + 8 columns, 4 power-iteration rounds) and a one-sided Jacobi
+ * SVD of the projected matrix, in float64: deterministic, and equal to an exact SVD's up to
+ * the bf16 rounding wherever singular value r stands clear of singular value r + 9.  Caller-
+ * owned host buffers; 1 <= rank <= min(N, K) else KQ_ERR_INVALID_ARG, non-finite weights
+ * KQ_ERR_INVALID_ARG, N K > 2^32 KQ_ERR_UNSUPPORTED.  Factor signs are arbitrary (the product
+ * is what counts). */
+kq_status kq_svdquant_factorize(const uint16_t* w_bf16, int64_t N, int64_t K, int rank,
+                                uint16_t* l_up_bf16, uint16_t* l_down_bf16,
+                                uint16_t* residual_bf16);
+kq_status kq_gemm_mxfp4_svdquant(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const uint8_t* r_codes, const uint8_t* r_scales, int64_t M,
+                                 int64_t N, int64_t K, const void* t_bf16,
+                                 const void* l_up_bf16, int rank, float* c_f32,
+                                 hipStream_t stream);
+kq_status kq_gemm_mxfp4_svdquant_bf16(const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const uint8_t* r_codes, const uint8_t* r_scales, int64_t M,
+                                      int64_t N, int64_t K, const void* t_bf16,
+                                      const void* l_up_bf16, int rank, void* c_bf16,
+                                      hipStream_t stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): kq_attn_quant_fwd_ws with the key-split workspace
  * taken from a static device array of the library instead of the caller.  Same arguments,

@@ -23,7 +23,9 @@ __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSE
            "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws",
            "kq_attn_quant_fwd_noalloc",
            "kq_attn_mxfp4_fwd", "kq_attn_r1_stats", "kq_attn_r1_amax", "kq_attn_r1_fwd",
-           "kq_gemm_fp8", "kq_gemm_mxfp4", "kq_gemm_fp8_bf16", "kq_gemm_mxfp4_bf16"]
+           "kq_gemm_fp8", "kq_gemm_mxfp4", "kq_gemm_fp8_bf16", "kq_gemm_mxfp4_bf16",
+           "kq_svdquant_down", "kq_gemm_mxfp4_svdquant", "kq_gemm_mxfp4_svdquant_bf16",
+           "kq_svdquant_factorize", "kq_svdquant_activations"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
 KQ_LAYOUT_ROWS = 0
@@ -71,6 +73,11 @@ _SIGNATURES = {
     "kq_gemm_mxfp4": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
     "kq_gemm_fp8_bf16": ([_P, _P, _I64, _I64, _I64, _F, _F, _P, _P], _I),
     "kq_gemm_mxfp4_bf16": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P], _I),
+    "kq_svdquant_down": ([_P, _P, _I64, _I64, _I, _P, _P], _I),
+    "kq_svdquant_factorize": ([_P, _I64, _I64, _I, _P, _P, _P], _I),
+    "kq_svdquant_activations": ([_P, _P, _I64, _I64, _I, _P, _P, _P, _P], _I),
+    "kq_gemm_mxfp4_svdquant": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I, _P, _P], _I),
+    "kq_gemm_mxfp4_svdquant_bf16": ([_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _I, _P, _P], _I),
 }
 
 
@@ -402,3 +409,81 @@ def kq_gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, stream=None):
 def kq_gemm_mxfp4_bf16(a_codes, a_scales, b_codes, b_scales, c, stream=None):
     """kq_gemm_mxfp4 with c bf16 [M, N]: each value the float32 result rounded once (RNE)."""
     _gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, c, True, stream)
+
+
+def kq_svdquant_down(a, l_down, t, stream=None):
+    """T = bf16(A L_down^T) for the SVD-Quant branch: a bf16 [M, K], l_down bf16 [r, K],
+    t bf16 [M, r]."""
+    import torch
+    M, K = a.shape
+    r = l_down.shape[0]
+    if l_down.dim() != 2 or l_down.shape[1] != K or tuple(t.shape) != (M, r):
+        raise KQError("expected a [M, K], l_down [r, K], t [M, r]")
+    _check(load().kq_svdquant_down(_dev(a, torch.bfloat16, "a"),
+                                   _dev(l_down, torch.bfloat16, "l_down"), M, K, r,
+                                   _dev(t, torch.bfloat16, "t"), _stream(stream)),
+           "kq_svdquant_down")
+
+
+def _gemm_svdquant(a_codes, a_scales, r_codes, r_scales, t, l_up, c, out_bf16, stream):
+    import torch
+    M, Kh = a_codes.shape
+    N = r_codes.shape[0]
+    K = 2 * Kh
+    rank = t.shape[1]
+    if (r_codes.dim() != 2 or r_codes.shape[1] != Kh or a_scales.numel() != M * (K // 32)
+            or r_scales.numel() != N * (K // 32) or tuple(c.shape) != (M, N)
+            or tuple(t.shape) != (M, rank) or tuple(l_up.shape) != (N, rank)):
+        raise KQError("expected codes [rows, K/2], scales [rows, K/32], t [M, r], l_up [N, r], "
+                      "c [M, N]")
+    fn = "kq_gemm_mxfp4_svdquant_bf16" if out_bf16 else "kq_gemm_mxfp4_svdquant"
+    _check(getattr(load(), fn)(
+        _dev(a_codes, torch.uint8, "a_codes"), _dev(a_scales, torch.uint8, "a_scales"),
+        _dev(r_codes, torch.uint8, "r_codes"), _dev(r_scales, torch.uint8, "r_scales"),
+        M, N, K, _dev(t, torch.bfloat16, "t"), _dev(l_up, torch.bfloat16, "l_up"), rank,
+        _dev(c, torch.bfloat16 if out_bf16 else torch.float32, "c"), _stream(stream)), fn)
+
+
+def kq_gemm_mxfp4_svdquant(a_codes, a_scales, r_codes, r_scales, t, l_up, c, stream=None):
+    """C = dq(a) dq(r)^T + t l_up^T: the MXFP4 GEMM of the activations and the SVD-Quant
+    residual plus the bf16 branch; c float32 [M, N]."""
+    _gemm_svdquant(a_codes, a_scales, r_codes, r_scales, t, l_up, c, False, stream)
+
+
+def kq_gemm_mxfp4_svdquant_bf16(a_codes, a_scales, r_codes, r_scales, t, l_up, c, stream=None):
+    """kq_gemm_mxfp4_svdquant with c bf16 [M, N]: each value the float32 result rounded once."""
+    _gemm_svdquant(a_codes, a_scales, r_codes, r_scales, t, l_up, c, True, stream)
+
+
+def kq_svdquant_factorize(w_bits, rank: int):
+    """Offline SVD-Quant weight step (host C code): from bf16 weights given as bit patterns
+    (numpy uint16 [N, K]), returns (l_up [N, r], l_down [r, K], residual [N, K]) as bf16 bit
+    patterns (numpy uint16)."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    if w.ndim != 2:
+        raise KQError("w must be [N, K]")
+    N, K = w.shape
+    l_up = np.empty((N, rank), np.uint16)
+    l_down = np.empty((rank, K), np.uint16)
+    res = np.empty((N, K), np.uint16)
+    _check(load().kq_svdquant_factorize(w.ctypes.data_as(_P), N, K, int(rank),
+                                        l_up.ctypes.data_as(_P), l_down.ctypes.data_as(_P),
+                                        res.ctypes.data_as(_P)), "kq_svdquant_factorize")
+    return l_up, l_down, res
+
+
+def kq_svdquant_activations(a, l_down, codes, scales, t, stream=None):
+    """One pass over the activations a (bf16 [M, K]): their MXFP4 codes (uint8 [M, K/2]) and
+    E8M0 scales (uint8 [M, K/32]), as kq_quantize_fp4_block, and T = bf16(a l_down^T)
+    (t bf16 [M, r], l_down bf16 [r, K])."""
+    import torch
+    M, K = a.shape
+    r = l_down.shape[0]
+    if (l_down.dim() != 2 or l_down.shape[1] != K or tuple(t.shape) != (M, r)
+            or codes.numel() != M * K // 2 or scales.numel() != M * K // 32):
+        raise KQError("expected a [M, K], l_down [r, K], codes [M, K/2], scales [M, K/32], "
+                      "t [M, r]")
+    _check(load().kq_svdquant_activations(
+        _dev(a, torch.bfloat16, "a"), _dev(l_down, torch.bfloat16, "l_down"), M, K, r,
+        _dev(codes, torch.uint8, "codes"), _dev(scales, torch.uint8, "scales"),
+        _dev(t, torch.bfloat16, "t"), _stream(stream)), "kq_svdquant_activations")

@@ -14,7 +14,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkq.so")
 ARCH = "gfx950"
 
-SOURCES = ["kq_api.cpp", "quant.hip", "attn_fp8.hip", "gemm.hip"]
+SOURCES = ["kq_api.cpp", "quant.hip", "attn_fp8.hip", "gemm.hip", "svdquant_host.cpp"]
 
 # Test-only probe of the matrix instructions' accumulation (tests/probe), built beside libkq.
 PROBE_SRC = os.path.join(ROOT, "tests", "probe", "mfma_probe.hip")

@@ -20,11 +20,18 @@
 // suffices; the HBM loads of a step are issued two steps before their LDS store (two register
 // sets), and the two waves of a SIMD hide each other's operand reads.
 //
+// SVD-Quant in FP4 (the same section names it beside PTQ in FP8 and FP4): the weights are
+// split offline into bf16 rank-r factors and a residual in MXFP4; per forward,
+// lowrank_down_kernel forms T = bf16(A L_down^T) [M][r], and the MXFP4 GEMM of A and the
+// residual starts its accumulators from T L_up^T (v_mfma_f32_32x32x16_bf16, whose 32 x 32
+// result layout is the f8f6f4 form's), so C = dq(A) dq(R)^T + T L_up^T in one pass.
+//
 // Operand layouts of the f8f6f4 MFMA (measured): for E4M3, lane (r, g) holds row r with
 // k = 16g .. 16g+15 in bytes 0-15 and k = 32+16g .. in bytes 16-31; for E2M1, lane (r, g)
 // holds k = 32g .. 32g+31 in 32 nibbles (low first) and supplies the scale of that 32-block.
 
 #include "kq_launch.h"
+#include "kq_fp4.h"
 
 namespace kq {
 namespace {
@@ -33,6 +40,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 256;            // workgroup tile of C (M and N)
 constexpr int kThreads = 512;         // 8 waves, two per SIMD
@@ -134,7 +142,7 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <bool kFP4, bool kBf16>
+template <bool kFP4, bool kBf16, bool kLowRank>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
   const int tiles_m = (p.m + kTile - 1) / kTile, tiles_n = (p.n + kTile - 1) / kTile;
@@ -205,6 +213,27 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[ni][mi][i] = 0.0f;
+  if constexpr (kLowRank) {
+    // SVD-Quant branch: acc = L_up T^T over the rank, 16 ranks per MFMA; lane (r, g) supplies
+    // row r (n for L_up, m for T) with ranks 16 s + 8 g .. + 7.  Rows past N or M read zeros.
+    const uint32_t rb = (uint32_t)p.rank * 2;
+    const __amdgpu_buffer_rsrc_t ur = make_rsrc(p.l_up, (uint32_t)p.n * rb);
+    const __amdgpu_buffer_rsrc_t tr = make_rsrc(p.t, (uint32_t)p.m * rb);
+    for (int s0 = 0; s0 < p.rank; s0 += 16) {
+      v8bf un[4], tm[2];
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        un[ni] = __builtin_bit_cast(v8bf, bload16(ur, (uint32_t)(nt * kTile + wn * 128 + 32 * ni + r) * rb + 2 * (s0 + 8 * g)));
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        tm[mi] = __builtin_bit_cast(v8bf, bload16(tr, (uint32_t)(mt * kTile + wm * 64 + 32 * mi + r) * rb + 2 * (s0 + 8 * g)));
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(un[ni], tm[mi], acc[ni][mi], 0, 0, 0);
+    }
+  }
 
   // Step s stores register set s % 2 (step s + 2, fetched in step s - 2) into stage (s + 2) % 3
   // (read last in step s - 1), fetches step s + 4 into the same set and multiplies stage s % 3
@@ -266,18 +295,158 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
 }
 
+// T = bf16(A L_down^T): A [M][K] bf16, L_down [rank][K] bf16, T [M][rank] bf16 (each value the
+// float32 sum rounded once, nearest even).  Workgroup = 8 waves = 32 rows of A (so an 8704-row
+// activation gives 272 workgroups, more than the compute units); the 8 waves split K into
+// consecutive ranges of whole 64-k groups and their partial sums meet in LDS.  A wave forms,
+// per chunk of 32 ranks, D = L_down_sub A_sub^T on v_mfma_f32_32x32x16_bf16 (lane (r, g) owns
+// row r and ranks 8q + 4g .. + 3 of the chunk).  In the 4 MFMAs of a 64-k group, lane (r, g)
+// supplies k = 64q + 32g .. + 31 (8 per MFMA), the same slots for both operands, so it streams
+// 64 contiguous bytes of its row per group (a wave reads whole 128-byte lines of A); the next
+// group's loads are issued before this group's MFMAs.  A is read once; L_down (rank x K) is
+// small and stays in the caches.  Rows past M and ranks past `rank` read zeros, are summed as
+// zeros and are not stored.
+// kQuant: the lane's 64 bytes of a group are exactly the 32-element FP4 block 2q + g of its row,
+// so the same pass also writes A's MXFP4 codes and E8M0 scales (the block quantizer's rule:
+// e = clamp(floor(log2 amax) - 2, -127, 127), E2M1 of x / 2^e by the hardware conversion).
+constexpr int kDownRanks = 64;    // at most 2 chunks of 32 ranks (64 KB of LDS for the sums)
+
+template <bool kQuant, int kNch>
+__global__ void __launch_bounds__(512) lowrank_down_kernel(const uint16_t* a, const uint16_t* l_down,
+                                                           int m, int k, int rank, uint16_t* t,
+                                                           uint4* a_codes, uint8_t* a_scales) {
+  extern __shared__ float red[];                    // [nch][16][8 waves][64 lanes]
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, g = l >> 5;
+  const int row = blockIdx.x * 32 + r;
+  const uint32_t kb = (uint32_t)k * 2;
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(a, (uint32_t)min(m, blockIdx.x * 32 + 32) * kb);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(l_down, (uint32_t)rank * kb);
+  constexpr int nch = kNch;            // chunks of 32 ranks
+  const int groups = k / 64, per = (groups + 7) / 8;
+  const int g0 = min(w * per, groups), g1 = min(g0 + per, groups);
+  v16f acc[kNch];
+#pragma unroll
+  for (int c = 0; c < kNch; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+  const uint32_t abase = (uint32_t)row * kb + 64 * g;
+  uint4 av[4], lv[kNch][4];
+#define KQ_DOWN_LOAD(G_)                                                                  \
+  {                                                                                       \
+    const uint32_t k2_ = 128u * (uint32_t)(G_);                                           \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) av[u] = bload16(ar, abase + k2_ + 16 * u); \
+    _Pragma("unroll") for (int c = 0; c < kNch; ++c)                           \
+      if (c < nch) {                                                                      \
+        const uint32_t lb_ = (uint32_t)(32 * c + r) * kb + 64 * g + k2_;                  \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) lv[c][u] = bload16(lr, lb_ + 16 * u); \
+      }                                                                                   \
+  }
+  if (g0 < g1) KQ_DOWN_LOAD(g0);
+  for (int gi = g0; gi < g1; ++gi) {
+    uint4 ac[4], lc[kNch][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ac[u] = av[u];
+#pragma unroll
+    for (int c = 0; c < kNch; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lc[c][u] = lv[c][u];
+    if (gi + 1 < g1) KQ_DOWN_LOAD(gi + 1);
+    if constexpr (kQuant) {
+      const uint32_t w[16] = {ac[0].x, ac[0].y, ac[0].z, ac[0].w, ac[1].x, ac[1].y, ac[1].z, ac[1].w,
+                              ac[2].x, ac[2].y, ac[2].z, ac[2].w, ac[3].x, ac[3].y, ac[3].z, ac[3].w};
+      u16x2 mx = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = mag_max(mx, w[j]);
+      const int e = mx_block_exponent(max((uint32_t)mx[0], (uint32_t)mx[1]) << 16);
+      const float sc = mx_scale_operand(e);
+      if (row < m) {
+        const int64_t blk = (int64_t)row * (k / 32) + 2 * gi + g;
+        a_codes[blk] = make_uint4(e2m1x8_bf16(w, sc), e2m1x8_bf16(w + 4, sc),
+                                  e2m1x8_bf16(w + 8, sc), e2m1x8_bf16(w + 12, sc));
+        a_scales[blk] = (uint8_t)(e + 127);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kNch; ++c)
+      if (c < nch) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lc[c][u]),
+                                                           __builtin_bit_cast(v8bf, ac[u]), acc[c], 0, 0, 0);
+      }
+  }
+#undef KQ_DOWN_LOAD
+  // the 8 waves' partial sums meet in LDS; thread tid then sums value (c, i) of lane l for
+  // (c, i, l) = its share of the nch x 16 x 64 results
+#pragma unroll
+  for (int c = 0; c < kNch; ++c)
+    if (c < nch)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[((c * 16 + i) * 8 + w) * 64 + l] = acc[c][i];
+  __syncthreads();
+  for (int e = tid; e < nch * 16 * 64; e += 512) {
+    const int ll = e & 63, ci = e >> 6, c = ci >> 4, i = ci & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) sum += red[(ci * 8 + ww) * 64 + ll];
+    red[(ci * 8) * 64 + ll] = sum;             // wave 0's slot holds the total
+    (void)c;
+    (void)i;
+  }
+  __syncthreads();
+  const int orow = blockIdx.x * 32 + (tid & 31), og = (tid >> 5) & 1;
+  if (tid >= 64 || orow >= m) return;
+  for (int c = 0; c < nch; ++c) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = 32 * c + 8 * q + 4 * og;
+      if (j < rank) {
+        float v[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = red[((c * 16 + 4 * q + x) * 8) * 64 + tid];
+        *reinterpret_cast<uint2*>(t + (int64_t)orow * rank + j) =
+            make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_lowrank_down(const uint16_t* a, const uint16_t* l_down, int m, int k, int rank,
+                               uint16_t* t, uint8_t* a_codes, uint8_t* a_scales,
+                               hipStream_t stream) {
+  const int blocks = (m + 31) / 32;
+  const size_t lds = (size_t)((rank + 31) / 32) * 16 * 8 * 64 * sizeof(float);
+  uint4* cv = reinterpret_cast<uint4*>(a_codes);
+  // one chunk of 32 ranks keeps the kernel within 128 registers: two workgroups per CU
+#define KQ_DOWN(Q, C)                                                                          \
+  hipLaunchKernelGGL((lowrank_down_kernel<Q, C>), dim3(blocks), dim3(512), lds, stream, a,     \
+                     l_down, m, k, rank, t, cv, a_scales)
+  if (a_codes != nullptr) {
+    if (rank <= 32) KQ_DOWN(true, 1); else KQ_DOWN(true, 2);
+  } else {
+    if (rank <= 32) KQ_DOWN(false, 1); else KQ_DOWN(false, 2);
+  }
+#undef KQ_DOWN
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmParams& p, bool fp4, hipStream_t stream) {
   const int tiles = ((p.m + kTile - 1) / kTile) * ((p.n + kTile - 1) / kTile);
-  if (fp4 && p.out_bf16)
-    hipLaunchKernelGGL((gemm_kernel<true, true>), dim3(tiles), dim3(kThreads), 0, stream, p);
+  const bool lr = p.rank > 0;
+  if (fp4 && lr && p.out_bf16)
+    hipLaunchKernelGGL((gemm_kernel<true, true, true>), dim3(tiles), dim3(kThreads), 0, stream, p);
+  else if (fp4 && lr)
+    hipLaunchKernelGGL((gemm_kernel<true, false, true>), dim3(tiles), dim3(kThreads), 0, stream, p);
+  else if (fp4 && p.out_bf16)
+    hipLaunchKernelGGL((gemm_kernel<true, true, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
   else if (fp4)
-    hipLaunchKernelGGL((gemm_kernel<true, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<true, false, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
   else if (p.out_bf16)
-    hipLaunchKernelGGL((gemm_kernel<false, true>), dim3(tiles), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<false, true, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<false, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<false, false, false>), dim3(tiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

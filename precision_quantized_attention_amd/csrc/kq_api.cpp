@@ -138,6 +138,9 @@ kq_status gemm_params(const uint8_t* a, const uint8_t* b, int64_t M, int64_t N, 
   p->a_scales = p->b_scales = nullptr;
   p->scale = 1.0f;
   p->out_bf16 = false;
+  p->rank = 0;
+  p->t = nullptr;
+  p->l_up = nullptr;
   return KQ_OK;
 }
 
@@ -348,6 +351,75 @@ kq_status kq_gemm_mxfp4_bf16(const uint8_t* a_codes, const uint8_t* a_scales,
                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t M,
                              int64_t N, int64_t K, void* c_bf16, hipStream_t stream) {
   return gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, M, N, K, c_bf16, true, stream);
+}
+
+static kq_status svdquant_pass(const void* a_bf16, const void* l_down_bf16, int64_t M, int64_t K,
+                               int rank, void* t_bf16, uint8_t* a_codes, uint8_t* a_scales,
+                               hipStream_t stream) {
+  if (a_bf16 == nullptr || l_down_bf16 == nullptr || t_bf16 == nullptr || M < 1 || K < 1 ||
+      rank < 1)
+    return KQ_ERR_INVALID_ARG;
+  if (!aligned(a_bf16, 16) || !aligned(l_down_bf16, 16) || !aligned(t_bf16, 16))
+    return KQ_ERR_INVALID_ARG;
+  if (K % 64 != 0 || rank % 16 != 0 || rank > 64) return KQ_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;           // 32-bit buffer ranges and offsets
+  if ((M + 32) * K * 2 >= lim || (int64_t)rank * K * 2 >= lim) return KQ_ERR_UNSUPPORTED;
+  return from_hip(kq::launch_lowrank_down(static_cast<const uint16_t*>(a_bf16),
+                                          static_cast<const uint16_t*>(l_down_bf16), (int)M,
+                                          (int)K, rank, static_cast<uint16_t*>(t_bf16), a_codes,
+                                          a_scales, stream));
+}
+
+kq_status kq_svdquant_down(const void* a_bf16, const void* l_down_bf16, int64_t M, int64_t K,
+                           int rank, void* t_bf16, hipStream_t stream) {
+  return svdquant_pass(a_bf16, l_down_bf16, M, K, rank, t_bf16, nullptr, nullptr, stream);
+}
+
+kq_status kq_svdquant_activations(const void* a_bf16, const void* l_down_bf16, int64_t M,
+                                  int64_t K, int rank, uint8_t* a_codes, uint8_t* a_scales,
+                                  void* t_bf16, hipStream_t stream) {
+  if (a_codes == nullptr || a_scales == nullptr || !aligned(a_codes, 16))
+    return KQ_ERR_INVALID_ARG;
+  return svdquant_pass(a_bf16, l_down_bf16, M, K, rank, t_bf16, a_codes, a_scales, stream);
+}
+
+static kq_status gemm_svdquant(const uint8_t* a_codes, const uint8_t* a_scales,
+                               const uint8_t* r_codes, const uint8_t* r_scales, int64_t M,
+                               int64_t N, int64_t K, const void* t_bf16, const void* l_up_bf16,
+                               int rank, void* c, bool out_bf16, hipStream_t stream) {
+  if (t_bf16 == nullptr || l_up_bf16 == nullptr || rank < 1) return KQ_ERR_INVALID_ARG;
+  if (!aligned(t_bf16, 16) || !aligned(l_up_bf16, 16)) return KQ_ERR_INVALID_ARG;
+  if (a_scales == nullptr || r_scales == nullptr) return KQ_ERR_INVALID_ARG;
+  if (!aligned(a_scales, 4) || !aligned(r_scales, 4)) return KQ_ERR_INVALID_ARG;
+  kq::GemmParams p;
+  const kq_status st = gemm_params(a_codes, r_codes, M, N, K, c, 128, K / 2, &p);
+  if (st != KQ_OK) return st;
+  if (rank % 16 != 0 || rank > 256) return KQ_ERR_UNSUPPORTED;
+  p.a_scales = a_scales;
+  p.b_scales = r_scales;
+  p.out_bf16 = out_bf16;
+  p.rank = rank;
+  p.t = static_cast<const uint16_t*>(t_bf16);
+  p.l_up = static_cast<const uint16_t*>(l_up_bf16);
+  return from_hip(kq::launch_gemm(p, true, stream));
+}
+
+kq_status kq_gemm_mxfp4_svdquant(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const uint8_t* r_codes, const uint8_t* r_scales, int64_t M,
+                                 int64_t N, int64_t K, const void* t_bf16,
+                                 const void* l_up_bf16, int rank, float* c_f32,
+                                 hipStream_t stream) {
+  return gemm_svdquant(a_codes, a_scales, r_codes, r_scales, M, N, K, t_bf16, l_up_bf16, rank,
+                       c_f32, false, stream);
+}
+
+kq_status kq_gemm_mxfp4_svdquant_bf16(const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const uint8_t* r_codes, const uint8_t* r_scales, int64_t M,
+                                      int64_t N, int64_t K, const void* t_bf16,
+                                      const void* l_up_bf16, int rank, void* c_bf16,
+                                      hipStream_t stream) {
+  return gemm_svdquant(a_codes, a_scales, r_codes, r_scales, M, N, K, t_bf16, l_up_bf16, rank,
+                       c_bf16, true, stream);
 }
 
 kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,

@@ -77,9 +77,20 @@ struct GemmParams {
   int m, n, k;
   float scale;              // s_a * s_b (FP8), 1 (FP4)
   bool out_bf16;            // C rounded to bf16 (round to nearest even) instead of float32
+  // SVD-Quant branch (FP4 only; rank 0: none): C += T L_up^T before the MXFP4 sum
+  int rank;                 // multiple of 16
+  const uint16_t* t;        // [M][rank] bf16
+  const uint16_t* l_up;     // [N][rank] bf16
 };
 
 // C = A B^T; K % 64 == 0 (FP8) or K % 128 == 0 (FP4), N % 4 == 0.
 hipError_t launch_gemm(const GemmParams& p, bool fp4, hipStream_t stream);
+
+// T = bf16(A L_down^T) for the SVD-Quant branch: A [m][k], L_down [rank][k], T [m][rank], all
+// bf16; k % 64 == 0, rank % 16 == 0, rank <= 64.  With a_codes (and a_scales) the same pass also
+// writes A's MXFP4 codes [m][k/2] and E8M0 scales [m][k/32] (kq_quantize_fp4_block's output).
+hipError_t launch_lowrank_down(const uint16_t* a, const uint16_t* l_down, int m, int k, int rank,
+                               uint16_t* t, uint8_t* a_codes, uint8_t* a_scales,
+                               hipStream_t stream);
 
 }  // namespace kq

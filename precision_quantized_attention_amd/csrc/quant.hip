@@ -15,6 +15,7 @@
 // mode is left at "preserve", so power-of-two rescaling stays exact.
 
 #include "kq_launch.h"
+#include "kq_fp4.h"
 
 #include <algorithm>
 
@@ -62,11 +63,6 @@ __device__ __forceinline__ uint2 e4m3x8(uint4 v, float inv) {
 // issues its atomic only if the stored maximum is below its own (the stored value only
 // grows, so skipping then changes nothing), which keeps the atomics on the one result word
 // few.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ u16x2 mag_max(u16x2 m, uint32_t w) {
-  return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
-}
 
 template <int kT, int kU>
 __global__ void __launch_bounds__(kT) amax_bf16_kernel(const uint16_t* __restrict__ x,
@@ -228,38 +224,6 @@ __global__ void __launch_bounds__(kThreads) fp8_transposed_kernel(const uint16_t
 // quad), and optionally 16 bytes of dequantized bf16 and 8 bytes of its per-tensor FP8.
 constexpr int kFp4U = 4;
 
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-
-// 8 values (4 bf16 pairs, or 8 floats) -> one dword of 8 E2M1 codes (byte i from pair i)
-__device__ __forceinline__ uint32_t e2m1x8_bf16(const uint32_t* w, float scale) {
-  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(v2bf, w[0]), scale, 0);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, w[1]), scale, 1);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, w[2]), scale, 2);
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, w[3]), scale, 3);
-}
-__device__ __forceinline__ uint32_t e2m1x8_f32(const float* f, float scale) {
-  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], scale, 0);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[2], f[3], scale, 1);
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[4], f[5], scale, 2);
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, f[6], f[7], scale, 3);
-}
-// one dword of 8 E2M1 codes -> 8 values times 2^e: as 4 bf16 pairs, or as 8 floats
-__device__ __forceinline__ uint4 e2m1x8_to_bf16(uint32_t c, float scale) {
-  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3)));
-}
-__device__ __forceinline__ void e2m1x8_to_f32(uint32_t c, float scale, float* f) {
-  const v2f a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 0);
-  const v2f b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 1);
-  const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 2);
-  const v2f h = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, scale, 3);
-  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-  f[4] = d[0]; f[5] = d[1]; f[6] = h[0]; f[7] = h[1];
-}
-
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
   return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // lane ^ 2
@@ -312,8 +276,8 @@ __global__ void __launch_bounds__(kThreads) fp4_block_kernel(
       am = max((uint32_t)m[0], (uint32_t)m[1]) << 16;
     }
     am = quad_max(am);
-    const int e = max((int)(am >> 23) - 129, -127);
-    const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+    const int e = mx_block_exponent(am);
+    const float scale = mx_scale_operand(e);
     uint32_t c;
     if constexpr (kRope) c = e2m1x8_f32(f, scale);
     else c = e2m1x8_bf16(w, scale);
