@@ -15,6 +15,7 @@ import precision_quantized_attention_amd as kq
 import workloads as W
 from kq_testutil import MAX_ABS_TOL, REL_L2_TOL, max_abs, rel_l2, sample_rows, to_dev
 from oracle import attention as A
+from oracle import formats as F
 from oracle import pipeline as OP
 from precision_quantized_attention_amd.pipeline import QuantizedSDPA
 
@@ -29,6 +30,19 @@ def _run(bits, mode="fp8", positions=None, stats=False):
     o = m.forward(*x)
     torch.cuda.synchronize()
     return m, o
+
+
+_QZ = {}
+
+
+def _oracle_inputs(cfg):
+    """The oracle's quantization of a workload, once per process (cfg 5's RoPE and FP4 steps
+    take tens of seconds)."""
+    if cfg not in _QZ:
+        c = W.config(cfg)
+        _QZ[cfg] = OP.quantize_inputs(*W.qkv_bits(cfg), mode=c.mode,
+                                      positions=W.positions(c) if c.rope else None)
+    return _QZ[cfg]
 
 
 def _check_codes(m, qz):
@@ -58,7 +72,7 @@ def test_attention_config(cfg):
     bits = W.qkv_bits(cfg)
     pos = W.positions(c) if c.rope else None
     m, o = _run(bits, mode=c.mode, positions=pos, stats=True)
-    qz = OP.quantize_inputs(*bits, mode=c.mode, positions=pos)
+    qz = _oracle_inputs(cfg)
     for n in "qkv":
         assert m.amax[n] == qz.amax[n] and m.scales[n] == qz.scale[n]
     _check_codes(m, qz)
@@ -90,6 +104,56 @@ def test_attention_config(cfg):
     ref64 = A.attention_fp64(sel[0], sel[1], sel[2], 1 / math.sqrt(128), rows=rows)
     print(f"cfg{cfg} vs unquantized fp64: rel_l2 {rel_l2(got, ref64[0]):.3e} "
           f"(oracle itself: {rel_l2(O[0], ref64[0]):.3e})", flush=True)
+
+
+_E4M3_POS = np.unique(F.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))    # 0 .. 448
+_MID = (_E4M3_POS[1:] + _E4M3_POS[:-1]) / 2
+
+
+def _near_ties(q8, k8, c1, rel=1e-5):
+    """Count of scores whose exact 448 p (R3, oracle definition) lies within `rel` of an E4M3
+    rounding midpoint: the elements whose code a float32-order difference could flip."""
+    raw = F.e4m3_decode(q8) @ F.e4m3_decode(k8).T
+    t = F.fl32(raw * float(c1)).astype(np.float64)
+    x = F.fl32(np.exp2(t - np.ceil(np.max(t, axis=1, keepdims=True)))).astype(np.float64) * 448.0
+    i = np.clip(np.searchsorted(_MID, x), 1, len(_MID) - 1)
+    d = np.minimum(np.abs(x - _MID[i]), np.abs(x - _MID[i - 1]))
+    return int(np.sum(d <= rel * x)), x.size
+
+
+@pytest.mark.parametrize("cfg,heads", [(2, None), (3, [(0, 0), (0, 23)]), (5, [(3, 23)])],
+                         ids=["cfg2-every-head", "cfg3-heads-0-and-23", "cfg5-b3-h23"])
+def test_attention_whole_heads(cfg, heads):
+    """Every query row of whole heads against the oracle (cfg 2: the whole tensor; cfg 3: head
+    0 and head 23, which runs entirely through the key split of the last round; cfg 5: the
+    last head of the last batch), with the gate on every element."""
+    c = W.config(cfg)
+    print(f"whole heads cfg{cfg} {c.name}", flush=True)
+    bits = W.qkv_bits(cfg)
+    pos = W.positions(c) if c.rope else None
+    m, o = _run(bits, mode=c.mode, positions=pos)
+    qz = _oracle_inputs(cfg)
+    _check_codes(m, qz)
+    heads = heads or [(b, h) for b in range(c.B) for h in range(c.H)]
+    o_np = o.cpu().numpy()
+    c1, _ = A.constants(qz.scale["q"][0], qz.scale["k"][0], qz.scale["v"][0], m.sm_scale)
+    worst, num, den, ties, n_el = 0.0, 0.0, 0.0, 0, 0
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        O, _, _ = A.attention_r3(qz.codes["q"][sl], qz.codes["k"][sl], qz.codes["v"][sl],
+                                 qz.scale["q"][0], qz.scale["k"][0], qz.scale["v"][0],
+                                 m.sm_scale)
+        d = o_np[b, h].astype(np.float64) - O[0, 0]
+        worst = max(worst, float(np.max(np.abs(d))))
+        num += float(np.sum(d ** 2))
+        den += float(np.sum(O[0, 0].astype(np.float64) ** 2))
+        if len(heads) <= 2 or h % 8 == 0:
+            t_, n_ = _near_ties(qz.codes["q"][b, h], qz.codes["k"][b, h], c1)
+            ties, n_el = ties + t_, n_el + n_
+    e = math.sqrt(num / den)
+    print(f"cfg{cfg} {len(heads)} whole heads: rel_l2 {e:.3e} max_abs {worst:.3e}; "
+          f"scores within 1e-5 of an E4M3 midpoint: {ties} of {n_el}", flush=True)
+    assert e <= REL_L2_TOL and worst <= MAX_ABS_TOL, (e, worst)
 
 
 @pytest.mark.parametrize("N", [1, 2, 5, 63, 64, 65, 127, 128, 129, 255, 257, 1000])

@@ -83,10 +83,14 @@ def _tie_allowance(q8, k8, v8, s_q, s_k, s_v, sm, amax_p, rows, rel=1e-5):
 
 def _compare(o_gpu, o_ref, label, allowance=0.0):
     e, a = rel_l2(o_gpu, o_ref), max_abs(o_gpu, o_ref)
-    excess = float(np.max(np.abs(np.asarray(o_gpu, np.float64) - o_ref) - allowance))
+    diff = np.abs(np.asarray(o_gpu, np.float64) - o_ref)
+    excess = float(np.max(diff - allowance))
+    over = int(np.sum(diff > MAX_ABS_TOL))           # elements that needed the allowance
+    used = float(np.max(np.where(diff > MAX_ABS_TOL, diff - MAX_ABS_TOL, 0.0)))
     print(f"{label}: rel_l2 {e:.3e} max_abs {a:.3e} (|O| max {np.abs(o_ref).max():.3g}; "
-          f"largest near-tie allowance {np.max(allowance):.3g}, max excess over it {excess:.3g})",
-          flush=True)
+          f"largest near-tie allowance {np.max(allowance):.3g}, max excess over it {excess:.3g}; "
+          f"elements past the plain 5e-2 gate: {over} of {diff.size} "
+          f"({100.0 * over / diff.size:.4f}%), by at most {used:.3g})", flush=True)
     assert e <= REL_L2_TOL, (label, e)
     assert excess <= MAX_ABS_TOL, (label, a, excess)
 
