@@ -71,8 +71,13 @@ def parse():
                     help="only the per-kernel quantizer timing (cache flushed before every "
                          "launch), one JSON line; the command profiled for the quantizer kernels")
     ap.add_argument("--pmc-workload", action="store_true",
-                    help="no timing: a plain copy of COPY_BYTES (counter calibration), then 3 "
-                         "steps; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+                    help="no timing: a plain copy of COPY_BYTES (counter calibration), then "
+                         "--pmc-steps steps; run under rocprofv3 --pmc")
+    ap.add_argument("--pmc-steps", type=int, default=3)
+    ap.add_argument("--pmc-summary", nargs="+", metavar=("KIND", "CSV"), default=None,
+                    help="no GPU: KIND 'traffic' or 'counters', then rocprofv3 "
+                         "counter_collection.csv files of --pmc-workload runs; prints the "
+                         "summary kept under profiles/")
     return ap.parse_args()
 
 
@@ -103,6 +108,100 @@ def traffic_bytes():
                    float(fields["attn_write_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
         return None
+
+
+def _short_kernel_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].split("::")[-1]
+
+
+def _read_counters(paths):
+    """{kernel: {counter: [value per dispatch]}} and {kernel: [duration ns per dispatch]}."""
+    import csv
+    vals, durs = {}, {}
+    for path in paths:
+        seen = set()
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = _short_kernel_name(r["Kernel_Name"])
+                vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+                key = (k, r["Dispatch_Id"])
+                if key not in seen:
+                    seen.add(key)
+                    durs.setdefault((path, k), []).append(
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return vals, durs
+
+
+def pmc_summary(kind, paths):
+    """Text summary of --pmc-workload counter runs (one rocprofv3 pass per CSV).
+
+    traffic: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel, scaled by what they
+    read for the plain 1 GiB copy that opens the run (the largest __amd_rocclr_copyBuffer
+    dispatch), as bytes per launch (median over dispatches).
+    counters: the attention kernel's SQ/GRBM counters (medians over the dispatches past the
+    first five, whose clock is still rising) and the figures derived from them."""
+    import statistics
+    vals, durs = _read_counters(paths)
+    med = lambda v: statistics.median(v[5:] if len(v) > 5 else v)
+    out = [f"kernel_sha: {kernel_sha()}"]
+    if kind == "traffic":
+        copy = vals["__amd_rocclr_copyBuffer"]
+        fscale = COPY_BYTES / (max(copy["FETCH_SIZE"]) * 1024) if "FETCH_SIZE" in copy else None
+        wscale = COPY_BYTES / (max(copy["WRITE_SIZE"]) * 1024) if "WRITE_SIZE" in copy else None
+        out += [f"copy_fetch_scale: {fscale:.4f}", f"copy_write_scale: {wscale:.4f}"]
+        for k in sorted(vals):
+            if not k.startswith(("attn", "amax", "fp8", "fp4")):
+                continue
+            name = "attn" if k.startswith("attn_fp8_kernel") else k.split("<")[0]
+            for ctr, sc, tag in (("FETCH_SIZE", fscale, "fetch"), ("WRITE_SIZE", wscale, "write")):
+                if ctr in vals[k]:
+                    out.append(f"{name}_{tag}_bytes_per_launch: "
+                               f"{round(med(vals[k][ctr]) * 1024 * sc)}")
+        return "\n".join(out)
+    # counters of the attention kernel
+    k = next(n for n in vals if n.startswith("attn_fp8_kernel"))
+    c = {ctr: med(v) for ctr, v in vals[k].items()}
+    dur_ns = statistics.median(d for (p, n), ds in durs.items() if n == k
+                               for d in (ds[5:] if len(ds) > 5 else ds))
+    xcds, cus, simds = 8, 256, 1024
+    cyc = c["GRBM_GUI_ACTIVE"] / xcds            # GRBM_GUI_ACTIVE is summed over the XCDs
+    out.append(f"kernel: {k}")
+    out.append(f"duration_us: {dur_ns / 1e3:.1f}")
+    for ctr in sorted(c):
+        out.append(f"{ctr}: {c[ctr]:.0f}")
+    out.append(f"gpu_clock_ghz: {cyc / dur_ns:.3f}  (GRBM_GUI_ACTIVE / {xcds} XCDs / duration)")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out.append(f"mfma_busy_pct: {100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * simds):.1f}"
+                   f"  (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {simds} SIMDs))")
+    if "SQ_ACTIVE_INST_VALU" in c:
+        out.append(f"valu_busy_pct: {100 * c['SQ_ACTIVE_INST_VALU'] / (cus * cyc):.1f}"
+                   f"  (SQ_ACTIVE_INST_VALU / {cus} CUs / cycles)")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out.append(f"valu_coexec_pct_of_mfma_busy: "
+                   f"{100 * c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}")
+    # per wave-tile (32 query rows x 64 keys) of the FLUX.1 Kontext workload the runs use
+    import workloads as W
+    w = W.config(3)
+    tiles = w.B * w.H * -(-w.N // 32) * -(-w.N // 64)
+    out.append(f"wave_tiles: {tiles}")
+    for ctr, tag in (("SQ_INSTS_VALU", "valu_insts"), ("SQ_INSTS_MFMA", "mfma_insts"),
+                     ("SQ_INSTS_VALU_TRANS_F32", "trans_insts"), ("SQ_INSTS_VALU_CVT", "cvt_insts"),
+                     ("SQ_INSTS_LDS", "lds_insts"), ("SQ_INSTS_SALU", "salu_insts")):
+        if ctr in c:
+            out.append(f"{tag}_per_wave_tile: {c[ctr] / tiles:.1f}")
+    if "SQ_ACTIVE_INST_VALU" in c:
+        out.append(f"valu_active_cycles_per_wave_tile: {4 * c['SQ_ACTIVE_INST_VALU'] / tiles:.0f}"
+                   f"  (SQ_ACTIVE_INST_VALU counts quad-cycles)")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out.append(f"mfma_busy_cycles_per_wave_tile: {c['SQ_VALU_MFMA_BUSY_CYCLES'] / tiles:.0f}")
+    out.append(f"simd_cycles_per_wave_tile: {cyc * simds / tiles:.0f}")
+    if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c:
+        out.append(f"lds_bank_conflict_pct: "
+                   f"{100 * c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.1f}"
+                   f"  (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)")
+    return "\n".join(out)
 
 
 def host_cpu() -> str:
@@ -303,10 +402,11 @@ def gemm_main(args):
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
-        for _ in range(3):
+        for _ in range(args.pmc_steps):
             step()
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_workload": shape.name, "copy_bytes": COPY_BYTES, "steps": 3}))
+        print(json.dumps({"pmc_workload": shape.name, "copy_bytes": COPY_BYTES,
+                          "steps": args.pmc_steps}))
         return
     ramp(step, args.ramp_seconds)
     for _ in range(args.warmup):
@@ -490,6 +590,9 @@ def quantizer_rates(c, q, k, v, m, stream, reps=20):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1:]))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1"}))
         sys.exit(2)
@@ -525,10 +628,11 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
-        for _ in range(3):
+        for _ in range(args.pmc_steps):
             m.forward(q, k, v)
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_workload": c.name, "copy_bytes": COPY_BYTES, "steps": 3}))
+        print(json.dumps({"pmc_workload": c.name, "copy_bytes": COPY_BYTES,
+                          "steps": args.pmc_steps}))
         return
 
     if args.quantizers:

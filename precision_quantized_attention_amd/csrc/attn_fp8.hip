@@ -174,6 +174,59 @@ __device__ __forceinline__ int krow_of_key(int kappa) {
   return 32 * ((kappa >> 4) & 1) + 8 * ((kappa >> 2) & 3) + 4 * ((kappa >> 5) & 1) + (kappa & 3);
 }
 
+// Work assignment over the 8 XCDs (dispatch slot y runs on XCD y mod 8, and each XCD has its
+// own L2).  Slots [0, nfull) are whole query blocks; the rem * split slots after them are key
+// ranges of the remaining rem blocks, numbered contiguously per XCD, and a block belongs to the
+// XCD that runs its first range.  Each XCD takes one contiguous range of logical blocks ((b, h)
+// major, query block minor): first the blocks of its whole-block slots, then the blocks it owns
+// among the split ones.  So the blocks of a head, and the key ranges of a split block, stay on
+// one XCD (exactly so when the counts divide by 8 and by the split) and share its copy of the
+// head's K and V.
+__device__ __forceinline__ int slots_on_xcd(int n, int x) { return (n - x + 7) >> 3; }
+
+struct XcdSplit {
+  int first_part;      // first key-range index of this XCD
+  int parts;           // key-range slots on this XCD
+  int owned;           // split blocks whose first range runs on this XCD
+  int logical0;        // first logical block of this XCD
+  int whole;           // whole-block slots on this XCD
+};
+
+__device__ __forceinline__ XcdSplit xcd_split(const AttnParams& a, int xcd) {
+  const int total = a.rem * a.split;
+  XcdSplit r{0, 0, 0, 0, 0};
+  for (int x = 0; x <= xcd; ++x) {
+    const int whole = slots_on_xcd(a.nfull, x);
+    const int parts = slots_on_xcd(a.nfull + total, x) - whole;
+    const int owned = a.split > 0 ? (r.first_part + parts + a.split - 1) / a.split -
+                                        (r.first_part + a.split - 1) / a.split
+                                  : 0;
+    if (x == xcd) {
+      r.parts = parts;
+      r.owned = owned;
+      r.whole = whole;
+      break;
+    }
+    r.first_part += parts;
+    r.logical0 += whole + owned;
+  }
+  return r;
+}
+
+// Logical block of split block blk (0 .. rem-1): the XCD whose key ranges hold its first one.
+__device__ __forceinline__ int split_block_logical(const AttnParams& a, int blk) {
+  const int first = blk * a.split, total = a.rem * a.split;
+  int first_part = 0, logical0 = 0;
+  for (int x = 0;; ++x) {
+    const int whole = slots_on_xcd(a.nfull, x);
+    const int parts = slots_on_xcd(a.nfull + total, x) - whole;
+    const int before = (first_part + a.split - 1) / a.split;   // blocks owned by earlier XCDs
+    if (first < first_part + parts || x == 7) return logical0 + whole + blk - before;
+    first_part += parts;
+    logical0 += whole + (first_part + a.split - 1) / a.split - before;
+  }
+}
+
 // Per-thread constants of a workgroup.
 struct Geo {
   __amdgpu_buffer_rsrc_t krs, vrs;   // K rows [N][128], V^T rows [128][ldv] of this (b, h)
@@ -237,6 +290,35 @@ __device__ __forceinline__ uint4 kread(const uint8_t* kt, int t) {
 }
 
 // Sets the scores of keys >= N to -inf; lane (r, g): s[kb][i] = key k0 + 32g + 16kb + i.
+// Two float32 values to E4M3 codes (round to nearest even) in the low or high 16 bits of old.
+// The scaled conversion with scale 1.0 returns the plain conversion's codes (checked on every
+// float32 in [-448, 448]) and issues at a higher rate.
+__device__ __forceinline__ int e4m3_pair(float a, float b, int old, bool hi) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2s r = hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old), a, b, 1.0f, true)
+                   : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old), a, b, 1.0f, false);
+  return __builtin_bit_cast(int, r);
+}
+
+// The 32 scores of a lane (s[0], s[1]) become exp2(arg(kb, s)), in place.  Each step issues the
+// argument of value t + 2 and the exp2 of value t, so a transcendental always has an
+// independent full-rate instruction beside it (a wave alone issues back-to-back exp2 at about
+// half the rate it issues them interleaved).
+template <class Arg>
+__device__ __forceinline__ void exp2_pipeline(v16f (&s)[2], Arg arg) {
+  s[0][0] = arg(0, s[0][0]);
+  s[0][1] = arg(0, s[0][1]);
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    if (t + 2 < 32) {
+      const int u = t + 2;
+      s[u >> 4][u & 15] = arg(u >> 4, s[u >> 4][u & 15]);
+    }
+    s[t >> 4][t & 15] = __builtin_amdgcn_exp2f(s[t >> 4][t & 15]);
+    KQ_FENCE();
+  }
+}
+
 __device__ __forceinline__ void mask_tail(v16f (&s)[2], int k0, const Geo& G) {
   const int nv = G.n - k0 - 32 * G.g;
 #pragma unroll
@@ -314,10 +396,10 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
       const int blk = t >> 3, i = 2 * (t & 7), w = 4 * blk + (i >> 2);
       const float p0 = pv[blk][i], p1 = pv[blk][i + 1];
       if ((i & 2) == 0) {
-        if (!kStats) pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], false);
+        if (!kStats) pop[w] = e4m3_pair(p0, p1, pop[w], false);
         pair = p0 + p1;
       } else {
-        if (!kStats) pop[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pop[w], true);
+        if (!kStats) pop[w] = e4m3_pair(p0, p1, pop[w], true);
         const float q4 = pair + (p0 + p1);
         if (blk) part1 = (i == 2) ? q4 : part1 + q4;
         else part0 = (i == 2) ? q4 : part0 + q4;
@@ -403,19 +485,14 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
     m_ref = m_top = G.m_fix;
     pscale = 127;
     d0o = d1o = 0.0f;
-    const float bias = G.lb_fix - G.m_fix;
+    const float bias = G.lb_fix - G.m_fix, m_fix = G.m_fix, lb_fix = G.lb_fix;
+    exp2_pipeline(s, [&](int, float x) {
+      return kWide ? unfused_arg(x, c1, m_fix, lb_fix) : __builtin_fmaf(x, c1, bias);
+    });
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int kb = h >> 1, i0 = 8 * (h & 1);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        s[kb][i0 + i] = kWide ? unfused_arg(s[kb][i0 + i], c1, G.m_fix, G.lb_fix)
-                              : __builtin_fmaf(s[kb][i0 + i], c1, bias);
-      KQ_FENCE();
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        s[kb][i0 + i] = fminf(__builtin_amdgcn_exp2f(s[kb][i0 + i]), 448.0f);
-    }
+      for (int i = 0; i < 16; ++i) s[kb][i] = fminf(s[kb][i], 448.0f);
     asm volatile("" ::"v"(s[0]), "v"(s[1]));
     return;
   }
@@ -448,20 +525,10 @@ __device__ __forceinline__ void valu_phase(int j, v16f (&s)[2], float mx0, float
   d0o = d0;
   d1o = d1;
   const float bias0 = kLog2_448 - mb0, bias1 = kLog2_448 - mb1;
-  // in place and in groups of 8, so that each exp2 issues eight instructions after the fma it
-  // reads (a shared temporary would chain all 64 instructions on their latencies)
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int kb = h >> 1, i0 = 8 * (h & 1);
-    const float bias = kb ? bias1 : bias0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      s[kb][i0 + i] = kWide ? unfused_arg(s[kb][i0 + i], c1, kb ? mb1 : mb0, kLog2_448)
-                            : __builtin_fmaf(s[kb][i0 + i], c1, bias);
-    KQ_FENCE();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[kb][i0 + i] = __builtin_amdgcn_exp2f(s[kb][i0 + i]);
-  }
+  exp2_pipeline(s, [&](int kb, float x) {
+    return kWide ? unfused_arg(x, c1, kb ? mb1 : mb0, kLog2_448)
+                 : __builtin_fmaf(x, c1, kb ? bias1 : bias0);
+  });
   // the values are consumed by the next matrix-core phase; keep them computed here
   asm volatile("" ::"v"(s[0]), "v"(s[1]));
 }
@@ -475,25 +542,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2 * (kFP4 ? kK4Stage : kKStage)];
   __shared__ __attribute__((aligned(16))) uint8_t Vs[2 * kVStage];   // FP8 V^T tiles
 
-  // Work assignment.  Dispatch slots below a.nfull are whole query blocks, in an XCD-aware
-  // order: consecutive slots go round-robin over the 8 XCDs, so each XCD gets a contiguous
-  // range of (head, query-block) pairs and keeps a head's K/V in its own L2.  The slots after
-  // them (dispatched last) are key ranges of the remaining query blocks.
+  // Work assignment (see xcd_split): slots below a.nfull are whole query blocks, the slots
+  // after them (dispatched last) key ranges of the remaining blocks.
   // (integer divisions run on the vector unit; readfirstlane returns the uniform results to
   // scalar registers so the buffer descriptors below stay scalar)
   const int N = a.n;
   const int ntiles_all = (N + kBN - 1) / kBN;
   const int bid = blockIdx.x;
   int logical, part = -1, t_begin = 0, t_end = ntiles_all;
+  const XcdSplit xs = xcd_split(a, bid & 7);
   if (bid < a.nfull) {
-    const int total = a.nfull;
-    const int xcd = bid & 7, local = bid >> 3, per = total >> 3, rm = total & 7;
-    logical = (xcd < rm) ? xcd * (per + 1) + local : rm * (per + 1) + (xcd - rm) * per + local;
+    logical = xs.logical0 + (bid >> 3);
   } else {
-    part = bid - a.nfull;
+    part = __builtin_amdgcn_readfirstlane(xs.first_part + (bid >> 3) - xs.whole);
     const int blk = __builtin_amdgcn_readfirstlane(part / a.split);
     const int chunk = part - blk * a.split;
-    logical = a.nfull + blk;
+    logical = split_block_logical(a, blk);
     t_begin = __builtin_amdgcn_readfirstlane(chunk * ntiles_all / a.split);
     t_end = __builtin_amdgcn_readfirstlane((chunk + 1) * ntiles_all / a.split);
   }
@@ -631,18 +695,56 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   // ---- epilogue: O = acc * s_v / sum(448 p); lane (r, g) holds d = 32c + 8(i/4) + 4g + i%4
   const float ltot = lsum + __shfl_xor(lsum, 32);      // sum of 448 p relative to m_ref
   const float m_row = fmaxf(m_top, __shfl_xor(m_top, 32));   // the row's M = ceil(max t)
+  // A wave's 32 x 128 float tile (o times `scale`) leaves through LDS, so that every store
+  // instruction writes whole 128-byte rows of a 32-column chunk, with the non-temporal hint:
+  // nothing here reads it again, and without the hint the 4 MB a round of blocks writes per
+  // XCD would push the next round's K and V out of the XCD's L2.  Row rr of the tile goes to
+  // dst + rr * kD (rows >= rows are skipped).  Each wave uses its own 4 KB of the K stages
+  // (callers pass a barrier first, after which no wave reads them): row rr of a chunk at
+  // rr * 128 bytes, 16-byte column j at (j ^ (rr & 7)).  The MXFP4 instance's K stages hold
+  // less than 32 KB; it stores directly.
+  constexpr bool kDirect = kFP4 || 2 * kKStage < kThreads / 64 * 4096;
+  auto store_tile = [&](float scale, float* dst, int rows) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    if constexpr (kDirect) {
+      if (r < rows) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f4v v = {o[c][4 * i4] * scale, o[c][4 * i4 + 1] * scale,
+                           o[c][4 * i4 + 2] * scale, o[c][4 * i4 + 3] * scale};
+            *reinterpret_cast<f4v*>(dst + (int64_t)r * kD + 32 * c + 8 * i4 + 4 * g) = v;
+          }
+      }
+    } else {
+      float* ws = reinterpret_cast<float*>(Ks + w * 4096);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int j = 2 * i4 + g;
+          const f4v v = {o[c][4 * i4] * scale, o[c][4 * i4 + 1] * scale,
+                         o[c][4 * i4 + 2] * scale, o[c][4 * i4 + 3] * scale};
+          *reinterpret_cast<f4v*>(ws + r * 32 + 4 * (j ^ (r & 7))) = v;
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int rr = 8 * h + (l >> 3), j = l & 7;
+          const f4v v = *reinterpret_cast<const f4v*>(ws + rr * 32 + 4 * (j ^ (rr & 7)));
+          if (rr < rows)
+            __builtin_nontemporal_store(v, reinterpret_cast<f4v*>(dst + (int64_t)rr * kD + 32 * c + 4 * j));
+        }
+      }
+    }
+  };
   if (part >= 0) {
     // partial result of a key range: the unnormalized accumulator and (m_ref, l, M, max raw
     // score); R1's first pass has no accumulator
     const int row = w * 32 + r;
     if (kMode != 1) {
-      float* wo = a.ws + ((int64_t)part * kBM + row) * kD;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<float4*>(wo + 32 * c + 8 * i4 + 4 * g) =
-              make_float4(o[c][4 * i4], o[c][4 * i4 + 1], o[c][4 * i4 + 2], o[c][4 * i4 + 3]);
+      __syncthreads();
+      store_tile(1.0f, a.ws + ((int64_t)part * kBM + w * 32) * kD, 32);
     }
     if (g == 0) {
       float* ws = a.ws + (int64_t)a.rem * a.split * kBM * kD + ((int64_t)part * kBM + row) * 4;
@@ -652,16 +754,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   }
   // R1 second pass: P was normalized before quantization, O = acc s_P s_V
   const float scale = kR1 ? a.r1_s_p * a.s_v : a.s_v / ltot;
-  if (q < N && a.o != nullptr) {
-    float* op = a.o + ((int64_t)bh * N + q) * kD;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float4 v = make_float4(o[c][4 * i4] * scale, o[c][4 * i4 + 1] * scale,
-                               o[c][4 * i4 + 2] * scale, o[c][4 * i4 + 3] * scale);
-        *reinterpret_cast<float4*>(op + 32 * c + 8 * i4 + 4 * g) = v;
-      }
+  if (kMode != 1 && a.o != nullptr) {
+    __syncthreads();
+    const int row0 = qb * kBM + w * 32;
+    store_tile(scale, a.o + ((int64_t)bh * N + row0) * kD, N - row0);
   }
   if (!kR1 && q < N && g == 0) {
     // (M, l) with l relative to the row's M
@@ -689,7 +785,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
   const int row_all = gid >> 5, d4 = 4 * (gid & 31);
   const int blk = row_all / kBM, row = row_all - blk * kBM;
   if (blk >= a.rem) return;
-  const int logical = a.nfull + blk;
+  const int logical = split_block_logical(a, blk);
   const int bh = logical / nqb, qb = logical - bh * nqb;
   const int q = qb * kBM + row;
   if (q >= a.n) return;

@@ -114,7 +114,40 @@ __global__ void __launch_bounds__(64) probe_kernel(const uint8_t* A, const uint8
   }
 }
 
+// Both float32 -> E4M3 conversions the attention kernel could use for P, on every float32 bit
+// pattern in [lo, lo + n): v_cvt_pk_fp8_f32 and v_cvt_scalef32_pk_fp8_f32 with scale 1.0, each
+// converting the pair (x, x).  Counts the patterns whose two results differ and keeps the
+// smallest such pattern (mismatch[0] = count, mismatch[1] = first pattern or 0xFFFFFFFF).
+__global__ void __launch_bounds__(256) cvt_probe_kernel(uint32_t lo, uint32_t n,
+                                                        unsigned int* mismatch) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  unsigned int count = 0, first = 0xFFFFFFFFu;
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) {
+    const uint32_t bits = lo + i;
+    const float x = __uint_as_float(bits);
+    const int plain = __builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false) & 0xFFFF;
+    const v2s sc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x, x, 1.0f, false);
+    const int scaled = (int)((uint32_t)(uint16_t)sc[0]);
+    if (plain != scaled) {
+      ++count;
+      first = bits < first ? bits : first;
+    }
+  }
+  if (count) {
+    atomicAdd(&mismatch[0], count);
+    atomicMin(&mismatch[1], first);
+  }
+}
+
 extern "C" {
+
+// Compares the two conversions on the bit patterns [lo, lo + n) (see cvt_probe_kernel);
+// mismatch is a device array of 2 words the caller sets to {0, 0xFFFFFFFF}.
+int cvt_probe_run(uint32_t lo, uint32_t n, unsigned int* mismatch, hipStream_t stream) {
+  if (mismatch == nullptr || n == 0 || (uint64_t)lo + n > (1ull << 32)) return -1;
+  hipLaunchKernelGGL(cvt_probe_kernel, dim3(2048), dim3(256), 0, stream, lo, n, mismatch);
+  return (int)hipGetLastError();
+}
 
 // Shape of a form: *m (= n) and *k; returns 0, or -1 for an unknown form.
 int mfma_probe_shape(int form, int* m, int* k) {

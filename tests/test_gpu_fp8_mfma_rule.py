@@ -235,3 +235,20 @@ def test_bf16_form_keeps_every_product():
     a, b = F.e4m3_decode(A), F.e4m3_decode(B)
     l1 = np.einsum("imk,ink->imn", np.abs(a), np.abs(b))
     assert np.all(np.abs(D - _exact(A, B)) <= 16 * 2.0 ** -24 * l1)
+
+
+def test_scaled_e4m3_conversion_equals_the_plain_one():
+    """The scaled float32 -> E4M3 pair conversion (scale 1.0) returns the plain conversion's
+    codes on every float32 in [-448, 448] (round to nearest even, both signs, subnormals), the
+    range the attention kernel converts 448 p in."""
+    lib = _probe()
+    lib.cvt_probe_run.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.cvt_probe_run.restype = ctypes.c_int
+    top = 0x43E00000                               # 448.0
+    for lo, n in ((0, top + 1), (0x80000000, top + 1)):
+        print(f"cvt probe [{lo:#x}, {lo + n:#x})", flush=True)
+        m = torch.tensor([0, -1], dtype=torch.int32, device="cuda")
+        assert lib.cvt_probe_run(lo, n, m.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        count, first = m.cpu().tolist()
+        assert count == 0, (count, hex(first & 0xFFFFFFFF))
