@@ -450,6 +450,41 @@ def gemm_main(args):
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None},
         "gemm_ms": round(kern_ms, 4),
     }
+    if args.gemm == "fp8" and not rank:
+        # the vendor library on the same codes and scales (hipBLASLt through torch._scaled_mm),
+        # timed the same way right after, alternating with this kernel; and whether its result
+        # equals this kernel's bit for bit
+        f8 = torch.float8_e4m3fn
+        a_f8, w_f8 = a8.view(f8), w8.view(f8)
+        s_a = torch.tensor(sa, dtype=torch.float32, device="cuda")
+        s_w = torch.tensor(sw, dtype=torch.float32, device="cuda")
+        odt = torch.bfloat16 if bf16_out else torch.float32
+        vendor = lambda: torch._scaled_mm(a_f8, w_f8.t(), scale_a=s_a, scale_b=s_w, out_dtype=odt)
+        try:
+            ref = vendor()
+            for _ in range(args.warmup):
+                vendor()
+            ours_us, theirs_us = [], []
+            for _ in range(3):
+                for fn, acc in ((launch, ours_us), (vendor, theirs_us)):
+                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                           for _ in range(args.steps)]
+                    for e0, e1 in evs:
+                        e0.record(stream)
+                        fn()
+                        e1.record(stream)
+                    torch.cuda.synchronize()
+                    acc.extend(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+            launch()
+            torch.cuda.synchronize()
+            out["vendor_gemm"] = {
+                "library": "hipBLASLt via torch._scaled_mm", "us": round(float(np.median(theirs_us)), 2),
+                "this_kernel_us": round(float(np.median(ours_us)), 2),
+                "ratio": round(float(np.median(ours_us) / np.median(theirs_us)), 4),
+                "bit_identical": bool(torch.equal(ref, c)),
+            }
+        except (RuntimeError, TypeError) as e:          # no FP8 GEMM in this torch build
+            out["vendor_gemm"] = {"error": str(e)[:200]}
     if rank:
         # the activation pass: A read once, its codes and scales and T written
         out["svdquant_activations_ms"] = round(down_ms, 4)

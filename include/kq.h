@@ -239,8 +239,11 @@ kq_status kq_attn_quant_fwd_noalloc(const uint8_t* q8, const uint8_t* k8, const 
  * q_codes, k_codes: device uint8 [B*H][N][64]; q_scales, k_scales: device uint8 [B*H][N][4]
  * (4-byte aligned); v8, v_layout, o_f32, row_stats_or_null as kq_attn_quant_fwd; workspace as
  * kq_attn_quant_fwd_ws (NULL: no key split; size from kq_attn_workspace_size).
- * Precondition: |t| < 2^20, which holds when sm_scale log2(e) 128 max|dq(q)| max|dq(k)| < 2^20
- * (the E8M0 scales are data, so the library cannot check it; beyond it p may overflow). */
+ * Precondition for parity with the definition: |t| < 2^20, which holds when
+ * sm_scale log2(e) 128 max|dq(q)| max|dq(k)| < 2^20 (the E8M0 scales are data, so the library
+ * cannot check it).  Beyond it the fused exp2 argument may put 448 p past the E4M3 range; the
+ * codes then saturate at 448 (no NaN while t is finite), and the output drifts from the
+ * definition. */
 kq_status kq_attn_mxfp4_fwd(const uint8_t* q_codes, const uint8_t* q_scales,
                             const uint8_t* k_codes, const uint8_t* k_scales, const uint8_t* v8,
                             int v_layout, int B, int H, int N, int d, float s_v, float sm_scale,

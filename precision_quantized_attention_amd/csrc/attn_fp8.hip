@@ -395,11 +395,15 @@ __device__ __forceinline__ void mfma_phase(int j, v16f (&sn)[2], const v16f (&pv
     {
       const int blk = t >> 3, i = 2 * (t & 7), w = 4 * blk + (i >> 2);
       const float p0 = pv[blk][i], p1 = pv[blk][i + 1];
+      // the native MXFP4 instance cannot bound |t| from its scales (they are data), and the
+      // fused exp2 argument may then put 448 p past 464, where E4M3 conversion gives NaN:
+      // its codes saturate at 448 instead
+      const float e0 = kFP4 ? fminf(p0, 448.0f) : p0, e1 = kFP4 ? fminf(p1, 448.0f) : p1;
       if ((i & 2) == 0) {
-        if (!kStats) pop[w] = e4m3_pair(p0, p1, pop[w], false);
+        if (!kStats) pop[w] = e4m3_pair(e0, e1, pop[w], false);
         pair = p0 + p1;
       } else {
-        if (!kStats) pop[w] = e4m3_pair(p0, p1, pop[w], true);
+        if (!kStats) pop[w] = e4m3_pair(e0, e1, pop[w], true);
         const float q4 = pair + (p0 + p1);
         if (blk) part1 = (i == 2) ? q4 : part1 + q4;
         else part0 = (i == 2) ? q4 : part0 + q4;

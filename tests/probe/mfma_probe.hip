@@ -139,7 +139,24 @@ __global__ void __launch_bounds__(256) cvt_probe_kernel(uint32_t lo, uint32_t n,
   }
 }
 
+// The two conversions of x[i] (as the pair (x, x)): the code bytes of each, for checking their
+// behaviour past the E4M3 range.
+__global__ void cvt_values_kernel(const float* x, uint8_t* plain, uint8_t* scaled, int n) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  plain[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x[i], x[i], 0, false) & 0xFF);
+  const v2s sc = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x[i], x[i], 1.0f, false);
+  scaled[i] = (uint8_t)((uint16_t)sc[0] & 0xFF);
+}
+
 extern "C" {
+
+int cvt_values_run(const float* x, uint8_t* plain, uint8_t* scaled, int n, hipStream_t stream) {
+  if (x == nullptr || plain == nullptr || scaled == nullptr || n < 1) return -1;
+  hipLaunchKernelGGL(cvt_values_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, x, plain, scaled, n);
+  return (int)hipGetLastError();
+}
 
 // Compares the two conversions on the bit patterns [lo, lo + n) (see cvt_probe_kernel);
 // mismatch is a device array of 2 words the caller sets to {0, 0xFFFFFFFF}.

@@ -175,3 +175,28 @@ def test_mxfp4_pipeline_refuses_out_of_range_scores():
         m.calibrate(*x)
     m8 = QuantizedSDPA(1, 2, 256, 128, mode="fp4")
     m8.calibrate(*x)                 # the FP8 BMM1 takes any finite scales
+
+
+def test_mxfp4_attention_past_the_precondition_stays_finite():
+    """The entry point itself, fed scales past its |t| < 2^20 precondition (E8M0 bytes up to
+    2^12, |t| up to ~2^33, still finite in float32): 448 p may leave the E4M3 range there, and
+    the codes saturate at 448, so every output is finite (the values themselves are not
+    compared: the fused exp2 argument no longer follows the definition)."""
+    print("mxfp4-bmm1 past the precondition", flush=True)
+    B, H, N = 1, 2, 320
+    rng = np.random.default_rng(91)
+    qc = rng.integers(0, 256, size=(B, H, N, 64), dtype=np.uint8)
+    kc = rng.integers(0, 256, size=(B, H, N, 64), dtype=np.uint8)
+    qs = rng.integers(127, 140, size=(B, H, N, 4), dtype=np.uint8)
+    ks = rng.integers(127, 140, size=(B, H, N, 4), dtype=np.uint8)
+    v8 = rng.integers(0, 0x7F, size=(B, H, N, 128), dtype=np.uint8)
+    sm = float(np.float32(1 / math.sqrt(128)))
+    vt = np.zeros((B * H, 128, kq.kq_vt_ld(N)), np.uint8)
+    vt[:, :, :N] = v8.reshape(B * H, N, 128).transpose(0, 2, 1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o = torch.empty((B, H, N, 128), dtype=torch.float32, device="cuda")
+    kq.kq_attn_mxfp4_fwd(dev(qc), dev(qs), dev(kc), dev(ks), dev(vt), 0.01, sm, o)
+    torch.cuda.synchronize()
+    # the largest |t| these scales allow: 6 * 6 * 2^12 * 2^12 * 128 * sm * log2(e)
+    print(f"  |t| bound {36 * 2.0 ** 24 * 128 * sm / math.log(2):.3g}", flush=True)
+    assert torch.isfinite(o).all()

@@ -252,3 +252,23 @@ def test_scaled_e4m3_conversion_equals_the_plain_one():
         torch.cuda.synchronize()
         count, first = m.cpu().tolist()
         assert count == 0, (count, hex(first & 0xFFFFFFFF))
+
+
+def test_scaled_e4m3_conversion_past_the_range():
+    """Past 448 both conversions agree and neither saturates: up to 464 (the midpoint to the
+    next, NaN, encoding) they round to 448 (code 0x7E / 0xFE), from there on they return the
+    NaN code 0x7F / 0xFF.  So a kernel whose 448 p can pass 464 must clamp it first."""
+    lib = _probe()
+    lib.cvt_values_run.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_void_p]
+    lib.cvt_values_run.restype = ctypes.c_int
+    xs = [448.0, 449.0, 463.9, 464.0, 480.0, 896.0, 1e6, 3.0e38, float("inf"),
+          -464.0, -1e6, -float("inf")]
+    x = torch.tensor(xs, dtype=torch.float32, device="cuda")
+    plain = torch.zeros(len(xs), dtype=torch.uint8, device="cuda")
+    scaled = torch.zeros(len(xs), dtype=torch.uint8, device="cuda")
+    assert lib.cvt_values_run(x.data_ptr(), plain.data_ptr(), scaled.data_ptr(), len(xs), None) == 0
+    torch.cuda.synchronize()
+    p, s = plain.cpu().tolist(), scaled.cpu().tolist()
+    print("x, plain, scaled:", [(v, hex(a), hex(b)) for v, a, b in zip(xs, p, s)], flush=True)
+    assert p == s
+    assert s == [0x7E] * 4 + [0x7F] * 5 + [0xFE, 0xFF, 0xFF], [hex(b) for b in s]
