@@ -296,107 +296,131 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 }
 
 // T = bf16(A L_down^T): A [M][K] bf16, L_down [rank][K] bf16, T [M][rank] bf16 (each value the
-// float32 sum rounded once, nearest even).  Workgroup = 8 waves = 32 rows of A (so an 8704-row
-// activation gives 272 workgroups, more than the compute units); the 8 waves split K into
-// consecutive ranges of whole 64-k groups and their partial sums meet in LDS.  A wave forms,
-// per chunk of 32 ranks, D = L_down_sub A_sub^T on v_mfma_f32_32x32x16_bf16 (lane (r, g) owns
-// row r and ranks 8q + 4g .. + 3 of the chunk).  In the 4 MFMAs of a 64-k group, lane (r, g)
-// supplies k = 64q + 32g .. + 31 (8 per MFMA), the same slots for both operands, so it streams
-// 64 contiguous bytes of its row per group (a wave reads whole 128-byte lines of A); the next
-// group's loads are issued before this group's MFMAs.  A is read once; L_down (rank x K) is
-// small and stays in the caches.  Rows past M and ranks past `rank` read zeros, are summed as
-// zeros and are not stored.
-// kQuant: the lane's 64 bytes of a group are exactly the 32-element FP4 block 2q + g of its row,
-// so the same pass also writes A's MXFP4 codes and E8M0 scales (the block quantizer's rule:
-// e = clamp(floor(log2 amax) - 2, -127, 127), E2M1 of x / 2^e by the hardware conversion).
-constexpr int kDownRanks = 64;    // at most 2 chunks of 32 ranks (64 KB of LDS for the sums)
+// float32 sum rounded once, nearest even).  Workgroup = 8 waves = 32 rows of A (an 8704-row
+// activation gives 272 workgroups, two per CU resident at once); the 8 waves split K into
+// consecutive ranges of whole 64-k groups and their partial sums meet in LDS at the end.
+// Per group a wave loads the 32 rows x 128 bytes of A and the chunks of 32 rows x 128 bytes of
+// L_down with whole-line loads (lane l takes row l / 8 + 8 j, 16-byte chunk l % 8), one group
+// ahead, writes them to its own LDS stage (rows padded to 144 bytes) and reads them back in the
+// MFMA layout: per chunk of 32 ranks, D = L_down_sub A_sub^T on v_mfma_f32_32x32x16_bf16, where
+// in MFMA u lane (r, g) supplies row r with k = 32 g + 8 u .. + 7 of the group, the same slots
+// for both operands (lane (r, g) owns output row r and ranks 8q + 4g .. + 3 of the chunk).
+// Only the wave itself touches its stage, and LDS serves a wave's accesses in order, so no
+// barrier is needed until the final sums.  Rows past M and ranks past `rank` read zeros
+// (buffer descriptors), are summed as zeros and are not stored.
+// kQuant: a lane's 16-byte chunk is a quarter of a 32-element FP4 block, the block's 4 lanes
+// are a quad, so the same pass writes A's MXFP4 codes (4 bytes per lane) and E8M0 scales (the
+// block quantizer's rule: e = clamp(floor(log2 amax) - 2, -127, 127), amax over the quad by
+// DPP, E2M1 of x / 2^e by the hardware conversion).
+constexpr int kDownPitch = 144;     // LDS row: 128 bytes of a group + 16 of padding
+constexpr int kDownStage = 32 * kDownPitch;
 
 template <bool kQuant, int kNch>
-__global__ void __launch_bounds__(512) lowrank_down_kernel(const uint16_t* a, const uint16_t* l_down,
-                                                           int m, int k, int rank, uint16_t* t,
-                                                           uint4* a_codes, uint8_t* a_scales) {
-  extern __shared__ float red[];                    // [nch][16][8 waves][64 lanes]
+__global__ void __launch_bounds__(512, 2) lowrank_down_kernel(const uint16_t* a, const uint16_t* l_down,
+                                                              int m, int k, int rank, uint16_t* t,
+                                                              uint32_t* a_codes, uint8_t* a_scales) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 31, g = l >> 5;
-  const int row = blockIdx.x * 32 + r;
+  const int lrow = l >> 3, lch = l & 7;                 // load mapping: rows lrow + 8 j, chunk lch
+  const int row0 = blockIdx.x * 32;
   const uint32_t kb = (uint32_t)k * 2;
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(a, (uint32_t)min(m, blockIdx.x * 32 + 32) * kb);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(a, (uint32_t)m * kb);
   const __amdgpu_buffer_rsrc_t lr = make_rsrc(l_down, (uint32_t)rank * kb);
-  constexpr int nch = kNch;            // chunks of 32 ranks
   const int groups = k / 64, per = (groups + 7) / 8;
   const int g0 = min(w * per, groups), g1 = min(g0 + per, groups);
+  uint8_t* sa = smem + w * (1 + kNch) * kDownStage;     // this wave's A stage, then its L stages
+  uint8_t* sl = sa + kDownStage;
   v16f acc[kNch];
 #pragma unroll
   for (int c = 0; c < kNch; ++c)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
-  const uint32_t abase = (uint32_t)row * kb + 64 * g;
-  uint4 av[4], lv[kNch][4];
-#define KQ_DOWN_LOAD(G_)                                                                  \
-  {                                                                                       \
-    const uint32_t k2_ = 128u * (uint32_t)(G_);                                           \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) av[u] = bload16(ar, abase + k2_ + 16 * u); \
-    _Pragma("unroll") for (int c = 0; c < kNch; ++c)                           \
-      if (c < nch) {                                                                      \
-        const uint32_t lb_ = (uint32_t)(32 * c + r) * kb + 64 * g + k2_;                  \
-        _Pragma("unroll") for (int u = 0; u < 4; ++u) lv[c][u] = bload16(lr, lb_ + 16 * u); \
-      }                                                                                   \
+  uint4 xa[4], xl[kNch][4];
+  const uint32_t aoff = (uint32_t)(row0 + lrow) * kb + 16 * lch;
+  const uint32_t loff = (uint32_t)lrow * kb + 16 * lch;
+#define KQ_DOWN_LOAD(G_)                                                                      \
+  {                                                                                           \
+    const uint32_t k2_ = 128u * (uint32_t)(G_);                                               \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) xa[j] = bload16(ar, aoff + 8 * j * kb + k2_); \
+    _Pragma("unroll") for (int c = 0; c < kNch; ++c)                                          \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                           \
+        xl[c][j] = bload16(lr, loff + (uint32_t)(32 * c + 8 * j) * kb + k2_);                 \
   }
-  if (g0 < g1) KQ_DOWN_LOAD(g0);
-  for (int gi = g0; gi < g1; ++gi) {
-    uint4 ac[4], lc[kNch][4];
+  // the waves of every workgroup would otherwise read the same L_down slice at the same
+  // moment (one L2 channel); each workgroup visits its range from a different group
+  const int ng = g1 - g0, rot = ng > 0 ? (int)(blockIdx.x % (unsigned)ng) : 0;
+  auto group_at = [&](int s_) { const int q_ = s_ + rot; return g0 + (q_ >= ng ? q_ - ng : q_); };
+  if (ng > 0) KQ_DOWN_LOAD(group_at(0));
+  for (int step = 0; step < ng; ++step) {
+    const int gi = group_at(step);
+    uint4 ca[4], cl[kNch][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ac[u] = av[u];
+    for (int j = 0; j < 4; ++j) ca[j] = xa[j];
 #pragma unroll
     for (int c = 0; c < kNch; ++c)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) lc[c][u] = lv[c][u];
-    if (gi + 1 < g1) KQ_DOWN_LOAD(gi + 1);
+      for (int j = 0; j < 4; ++j) cl[c][j] = xl[c][j];
+    if (step + 1 < ng) KQ_DOWN_LOAD(group_at(step + 1));
     if constexpr (kQuant) {
-      const uint32_t w[16] = {ac[0].x, ac[0].y, ac[0].z, ac[0].w, ac[1].x, ac[1].y, ac[1].z, ac[1].w,
-                              ac[2].x, ac[2].y, ac[2].z, ac[2].w, ac[3].x, ac[3].y, ac[3].z, ac[3].w};
-      u16x2 mx = {0, 0};
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = mag_max(mx, w[j]);
-      const int e = mx_block_exponent(max((uint32_t)mx[0], (uint32_t)mx[1]) << 16);
-      const float sc = mx_scale_operand(e);
-      if (row < m) {
-        const int64_t blk = (int64_t)row * (k / 32) + 2 * gi + g;
-        a_codes[blk] = make_uint4(e2m1x8_bf16(w, sc), e2m1x8_bf16(w + 4, sc),
-                                  e2m1x8_bf16(w + 8, sc), e2m1x8_bf16(w + 12, sc));
-        a_scales[blk] = (uint8_t)(e + 127);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t wv[4] = {ca[j].x, ca[j].y, ca[j].z, ca[j].w};
+        u16x2 mx = {0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mx = mag_max(mx, wv[q]);
+        const uint32_t am = quad_max(max((uint32_t)mx[0], (uint32_t)mx[1]));
+        const int e = mx_block_exponent(am << 16);
+        const int row = row0 + lrow + 8 * j;
+        if (row < m) {
+          a_codes[(int64_t)row * (k / 8) + 8 * gi + lch] = e2m1x8_bf16(wv, mx_scale_operand(e));
+          if ((lch & 3) == 0) a_scales[(int64_t)row * (k / 32) + 2 * gi + (lch >> 2)] = (uint8_t)(e + 127);
+        }
       }
     }
 #pragma unroll
-    for (int c = 0; c < kNch; ++c)
-      if (c < nch) {
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<uint4*>(sa + (lrow + 8 * j) * kDownPitch + 16 * lch) = ca[j];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lc[c][u]),
-                                                           __builtin_bit_cast(v8bf, ac[u]), acc[c], 0, 0, 0);
-      }
+      for (int c = 0; c < kNch; ++c)
+        *reinterpret_cast<uint4*>(sl + c * kDownStage + (lrow + 8 * j) * kDownPitch + 16 * lch) = cl[c][j];
+    }
+    uint4 av[4], lv[kNch][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = *reinterpret_cast<const uint4*>(sa + r * kDownPitch + 16 * (4 * g + u));
+#pragma unroll
+      for (int c = 0; c < kNch; ++c)
+        lv[c][u] = *reinterpret_cast<const uint4*>(sl + c * kDownStage + r * kDownPitch + 16 * (4 * g + u));
+    }
+#pragma unroll
+    for (int c = 0; c < kNch; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, lv[c][u]),
+                                                         __builtin_bit_cast(v8bf, av[u]), acc[c], 0, 0, 0);
   }
 #undef KQ_DOWN_LOAD
-  // the 8 waves' partial sums meet in LDS; thread tid then sums value (c, i) of lane l for
-  // (c, i, l) = its share of the nch x 16 x 64 results
+  // the 8 waves' partial sums meet in LDS (the stages are no longer read after the barrier);
+  // thread tid then sums value (c, i) of lane l for (c, i, l) = its share of the
+  // kNch x 16 x 64 results
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);          // [kNch][16][8 waves][64 lanes]
 #pragma unroll
   for (int c = 0; c < kNch; ++c)
-    if (c < nch)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[((c * 16 + i) * 8 + w) * 64 + l] = acc[c][i];
+    for (int i = 0; i < 16; ++i) red[((c * 16 + i) * 8 + w) * 64 + l] = acc[c][i];
   __syncthreads();
-  for (int e = tid; e < nch * 16 * 64; e += 512) {
-    const int ll = e & 63, ci = e >> 6, c = ci >> 4, i = ci & 15;
+  for (int e = tid; e < kNch * 16 * 64; e += 512) {
+    const int ll = e & 63, ci = e >> 6;
     float sum = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < 8; ++ww) sum += red[(ci * 8 + ww) * 64 + ll];
     red[(ci * 8) * 64 + ll] = sum;             // wave 0's slot holds the total
-    (void)c;
-    (void)i;
   }
   __syncthreads();
-  const int orow = blockIdx.x * 32 + (tid & 31), og = (tid >> 5) & 1;
+  const int orow = row0 + (tid & 31), og = (tid >> 5) & 1;
   if (tid >= 64 || orow >= m) return;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = 0; c < kNch; ++c) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int j = 32 * c + 8 * q + 4 * og;
@@ -417,16 +441,19 @@ hipError_t launch_lowrank_down(const uint16_t* a, const uint16_t* l_down, int m,
                                uint16_t* t, uint8_t* a_codes, uint8_t* a_scales,
                                hipStream_t stream) {
   const int blocks = (m + 31) / 32;
-  const size_t lds = (size_t)((rank + 31) / 32) * 16 * 8 * 64 * sizeof(float);
-  uint4* cv = reinterpret_cast<uint4*>(a_codes);
-  // one chunk of 32 ranks keeps the kernel within 128 registers: two workgroups per CU
+  const int nch = (rank + 31) / 32;
+  // per wave one A stage and nch L stages; the final sums reuse the same memory
+  const size_t stages = (size_t)8 * (1 + nch) * kDownStage;
+  const size_t sums = (size_t)nch * 16 * 8 * 64 * sizeof(float);
+  const size_t lds = stages > sums ? stages : sums;
+  uint32_t* cv = reinterpret_cast<uint32_t*>(a_codes);
 #define KQ_DOWN(Q, C)                                                                          \
   hipLaunchKernelGGL((lowrank_down_kernel<Q, C>), dim3(blocks), dim3(512), lds, stream, a,     \
                      l_down, m, k, rank, t, cv, a_scales)
   if (a_codes != nullptr) {
-    if (rank <= 32) KQ_DOWN(true, 1); else KQ_DOWN(true, 2);
+    if (nch == 1) KQ_DOWN(true, 1); else KQ_DOWN(true, 2);
   } else {
-    if (rank <= 32) KQ_DOWN(false, 1); else KQ_DOWN(false, 2);
+    if (nch == 1) KQ_DOWN(false, 1); else KQ_DOWN(false, 2);
   }
 #undef KQ_DOWN
   return hipGetLastError();

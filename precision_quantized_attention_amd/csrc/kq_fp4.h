@@ -50,6 +50,13 @@ __device__ __forceinline__ void e2m1x8_to_f32(uint32_t c, float scale, float* f)
   f[4] = d[0]; f[5] = d[1]; f[6] = h[0]; f[7] = h[1];
 }
 
+// max of v over the 4 lanes of a quad (lanes 4j .. 4j+3), in every lane of it: two DPP
+// quad-permute steps (lane ^ 1, then lane ^ 2)
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+}
+
 // The MX block exponent of a 32-element block from its largest magnitude as float32 bits:
 // e = clamp(floor(log2 amax) - 2, -127, 127) (a zero or subnormal amax gives -127), and the
 // conversions' scale operand 2^e as the float with exponent field e + 127.

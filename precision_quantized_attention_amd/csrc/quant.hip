@@ -224,11 +224,6 @@ __global__ void __launch_bounds__(kThreads) fp8_transposed_kernel(const uint16_t
 // quad), and optionally 16 bytes of dequantized bf16 and 8 bytes of its per-tensor FP8.
 constexpr int kFp4U = 4;
 
-__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
-  return max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // lane ^ 2
-}
-
 template <bool kRope, bool kDq, bool kFp8>
 __global__ void __launch_bounds__(kThreads) fp4_block_kernel(
     const uint4* __restrict__ x, int64_t n16, uint32_t* __restrict__ codes,
