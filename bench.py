@@ -74,6 +74,10 @@ def parse():
                     help="no timing: a plain copy of COPY_BYTES (counter calibration), then "
                          "--pmc-steps steps; run under rocprofv3 --pmc")
     ap.add_argument("--pmc-steps", type=int, default=3)
+    ap.add_argument("--trace-summary", nargs="+", metavar=("CSV", "SKIP"), default=None,
+                    help="no GPU: a rocprofv3 kernel_trace.csv (and optionally how many first "
+                         "calls of each kernel to drop as warm-up); prints per-kernel "
+                         "statistics and the kernel sources' digests")
     ap.add_argument("--pmc-summary", nargs="+", metavar=("KIND", "CSV"), default=None,
                     help="no GPU: KIND 'traffic' or 'counters', then rocprofv3 "
                          "counter_collection.csv files of --pmc-workload runs; prints the "
@@ -132,6 +136,41 @@ def _read_counters(paths):
                     durs.setdefault((path, k), []).append(
                         int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return vals, durs
+
+
+def source_sha(name: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, "precision_quantized_attention_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def trace_summary(path, skip=0):
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace CSV (microseconds), with the
+    digests of the kernel sources; with skip > 0 also each kernel's statistics past its first
+    `skip` calls."""
+    import csv
+    import statistics
+    d = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            name = name.split("(")[0] if not name.startswith("void at::") else name[:60]
+            d.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    tot = sum(sum(v) for v in d.values())
+    out = [f"# kernel sources sha256[:16]: attn_fp8.hip {source_sha('attn_fp8.hip')}, "
+           f"gemm.hip {source_sha('gemm.hip')}, quant.hip {source_sha('quant.hip')}",
+           f"{'kernel':62s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>8s} "
+           f"{'max_us':>8s} {'pct':>6s}"]
+    for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{k[:62]:62s} {len(v):6d} {statistics.mean(v):9.2f} {statistics.median(v):9.2f} "
+                   f"{min(v):8.2f} {max(v):8.2f} {100 * sum(v) / tot:6.2f}")
+    if skip:
+        for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+            if len(v) > skip:
+                w = v[skip:]
+                out.append(f"# {k[:62]}: past its first {skip} calls, {len(w)} calls, mean "
+                           f"{statistics.mean(w):.2f} us, median {statistics.median(w):.2f} us")
+    return "\n".join(out)
 
 
 def pmc_summary(kind, paths):
@@ -627,6 +666,10 @@ def main():
     args = parse()
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1:]))
+        return
+    if args.trace_summary:
+        skip = int(args.trace_summary[1]) if len(args.trace_summary) > 1 else 0
+        print(trace_summary(args.trace_summary[0], skip))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1"}))
