@@ -144,10 +144,20 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def trace_summary(path, skip=0):
+# algorithmic bytes per element of each quantizer kernel (inputs read once, outputs written
+# once): bf16 in; FP8 out 1; FP4 codes 0.5 + E8M0 1/32; fused FP8 1; dequantized bf16 2
+QUANT_BYTES = {"amax_bf16_kernel": 2.0, "fp8_rows_kernel": 3.0, "fp8_transposed_kernel": 3.0,
+               "fp4_block_kernel<false, false, false>": 2.53125,
+               "fp4_block_kernel<false, false, true>": 3.53125,
+               "fp4_block_kernel<false, true, false>": 4.53125,
+               "fp4_block_kernel<true, false, true>": 3.53125}
+
+
+def trace_summary(path, skip=0, elements=0):
     """Per-kernel duration statistics of a rocprofv3 --kernel-trace CSV (microseconds), with the
     digests of the kernel sources; with skip > 0 also each kernel's statistics past its first
-    `skip` calls."""
+    `skip` calls; with elements > 0 the GB/s of each quantizer kernel on a tensor of that many
+    elements (algorithmic bytes / median duration)."""
     import csv
     import statistics
     d = {}
@@ -170,6 +180,18 @@ def trace_summary(path, skip=0):
                 w = v[skip:]
                 out.append(f"# {k[:62]}: past its first {skip} calls, {len(w)} calls, mean "
                            f"{statistics.mean(w):.2f} us, median {statistics.median(w):.2f} us")
+    if elements:
+        out.append(f"# GB/s = {elements} elements x bytes per element / median duration "
+                   f"(HBM peak {HBM_PEAK_GBS:.0f})")
+        for k, v in d.items():
+            base = k.replace("void ", "").split("::")[-1]
+            b = next((b for pat, b in QUANT_BYTES.items()
+                      if base == pat or ("<" not in pat and base.split("<")[0] == pat)), None)
+            if b is not None:
+                med = statistics.median(v)
+                gbs = elements * b / (med * 1e-6) / 1e9
+                out.append(f"{k[:62]:62s} {b:7.4f} B/elem {gbs:8.1f} GB/s "
+                           f"{100 * gbs / HBM_PEAK_GBS:5.1f}%")
     return "\n".join(out)
 
 
@@ -669,7 +691,8 @@ def main():
         return
     if args.trace_summary:
         skip = int(args.trace_summary[1]) if len(args.trace_summary) > 1 else 0
-        print(trace_summary(args.trace_summary[0], skip))
+        elements = int(args.trace_summary[2]) if len(args.trace_summary) > 2 else 0
+        print(trace_summary(args.trace_summary[0], skip, elements))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1"}))

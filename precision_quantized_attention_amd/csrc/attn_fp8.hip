@@ -701,8 +701,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
   const float m_row = fmaxf(m_top, __shfl_xor(m_top, 32));   // the row's M = ceil(max t)
   // A wave's 32 x 128 float tile (o times `scale`) leaves through LDS, so that every store
   // instruction writes whole 128-byte rows of a 32-column chunk, with the non-temporal hint:
-  // nothing here reads it again, and without the hint the 4 MB a round of blocks writes per
-  // XCD would push the next round's K and V out of the XCD's L2.  Row rr of the tile goes to
+  // without it the 4 MB of O a round of blocks writes per XCD pushes the next round's K and V
+  // out of the XCD's L2 (the split ranges' partials as well: the merge kernel then reads them
+  // from HBM, which costs it less than the K and V fetched again cost here).  Row rr of the
+  // tile goes to
   // dst + rr * kD (rows >= rows are skipped).  Each wave uses its own 4 KB of the K stages
   // (callers pass a barrier first, after which no wave reads them): row rr of a chunk at
   // rr * 128 bytes, 16-byte column j at (j ^ (rr & 7)).  The MXFP4 instance's K stages hold
@@ -785,9 +787,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
 // R1: the second pass's parts share the row's M, and O = acc s_P s_v; the first pass has no
 // accumulator and writes the (M, l, max p) statistics.
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb) {
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int row_all = gid >> 5, d4 = 4 * (gid & 31);
-  const int blk = row_all / kBM, row = row_all - blk * kBM;
+  // a workgroup covers 8 rows of one query block (32 threads per row, kBM rows per block), so
+  // the block and its logical index are uniform: scalar arithmetic
+  static_assert(kBM % 8 == 0, "a combine workgroup must stay inside one query block");
+  const int blk = (int)blockIdx.x / (kBM / 8);
+  const int row = ((int)blockIdx.x - blk * (kBM / 8)) * 8 + (int)(threadIdx.x >> 5);
+  const int d4 = 4 * (threadIdx.x & 31);
   if (blk >= a.rem) return;
   const int logical = split_block_logical(a, blk);
   const int bh = logical / nqb, qb = logical - bh * nqb;
@@ -795,6 +800,18 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
   if (q >= a.n) return;
   const float4* st = reinterpret_cast<const float4*>(a.ws + (int64_t)a.rem * a.split * kBM * kD) +
                      (int64_t)blk * a.split * kBM + row;
+  // the partials of up to kBatch ranges are loaded together, the first batch with the
+  // statistics, so a typical split (<= kBatch ranges) costs one round trip to memory; the sums
+  // still run over the ranges in order
+  constexpr int kBatch = 8;
+  const bool want_o = a.o != nullptr;
+  const float* pb = a.ws + ((int64_t)blk * a.split * kBM + row) * kD + d4;
+  const int64_t pstride = (int64_t)kBM * kD;
+  float4 x[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+    x[u] = (want_o && u < a.split) ? *reinterpret_cast<const float4*>(pb + u * pstride)
+                                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float R = -INFINITY, m_row = -INFINITY, rmax = -INFINITY;
   for (int s = 0; s < a.split; ++s) {
     const float4 v = st[(int64_t)s * kBM];
@@ -804,17 +821,24 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnParams a, int nqb
   }
   float l = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int s = 0; s < a.split; ++s) {
-    const float4 v = st[(int64_t)s * kBM];
-    const float f = __builtin_amdgcn_ldexpf(1.0f, (int)(v.x - R));
-    l += v.y * f;
-    if (a.o != nullptr) {
-      const float4 x = *reinterpret_cast<const float4*>(
-          a.ws + (((int64_t)blk * a.split + s) * kBM + row) * kD + d4);
-      acc.x += x.x * f;
-      acc.y += x.y * f;
-      acc.z += x.z * f;
-      acc.w += x.w * f;
+  for (int s0 = 0; s0 < a.split; s0 += kBatch) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (want_o && s0 + u < a.split)
+          x[u] = *reinterpret_cast<const float4*>(pb + (s0 + u) * pstride);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (s0 + u < a.split) {
+        const float4 v = st[(int64_t)(s0 + u) * kBM];
+        const float f = __builtin_amdgcn_ldexpf(1.0f, (int)(v.x - R));
+        l += v.y * f;
+        acc.x += x[u].x * f;
+        acc.y += x[u].y * f;
+        acc.z += x[u].z * f;
+        acc.w += x[u].w * f;
+      }
     }
   }
   if (a.o != nullptr) {
