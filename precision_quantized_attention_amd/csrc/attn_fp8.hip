@@ -125,6 +125,13 @@ __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   return make_uint2(v[0], v[1]);
 }
+// The same with the non-temporal cache policy (aux bit 1): for data read once per workgroup
+// (Q), which would otherwise take L2 space from the K and V tiles every workgroup of the XCD
+// reads.
+__device__ __forceinline__ uint2 bload8_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
+  return make_uint2(v[0], v[1]);
+}
 
 // 4 E4M3 codes (one dword) -> 4 bf16 values (two dwords), exact.
 __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
@@ -588,7 +595,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     const uint32_t qo = (uint32_t)q * kD + 8 * g;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const uint2 c = bload8(qr, qo + 16 * m);
+      const uint2 c = bload8_stream(qr, qo + 16 * m);
       const uint2 lo = e4m3x4_to_bf16(c.x), hi = e4m3x4_to_bf16(c.y);
       qop.v[m] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
