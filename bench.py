@@ -68,8 +68,8 @@ def parse():
     ap.add_argument("--gemm-out", choices=["f32", "bf16"], default="f32",
                     help="C in float32 (kq_gemm_*) or bf16 (kq_gemm_*_bf16)")
     ap.add_argument("--quantizers", action="store_true",
-                    help="only the per-kernel quantizer timing (cache flushed before every "
-                         "launch), one JSON line; the command profiled for the quantizer kernels")
+                    help="only the per-kernel quantizer timing (inputs read from HBM: copies in "
+                         "rotation), one JSON line; the command profiled for the quantizer kernels")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="no timing: a plain copy of COPY_BYTES (counter calibration), then "
                          "--pmc-steps steps; run under rocprofv3 --pmc")
@@ -632,55 +632,82 @@ def ramp(step, seconds):
             return n, time.perf_counter() - t0
 
 
-def quantizer_rates(c, q, k, v, m, stream, reps=20):
-    """Each quantizer and calibration kernel of the workload launched alone with the 256 MB
-    last-level cache flushed before every launch (a 512 MB write), timed with HIP events on its
-    stream: microseconds (median) and GB/s of algorithmic bytes (inputs read once, outputs
-    written once).  The FP4 encoder is also timed on the FP8 workloads' Q (codes + scales, and
-    with the fused FP8 output), as the encoder of the FP4 variant on the same tensor size."""
+def cold_launch_us(fns, stream, rounds=3, repeats=5):
+    """Mean duration in microseconds of one launch that reads its inputs from HBM.  Each of
+    `fns` works on its own copy of the inputs and outputs, the copies together well above the
+    256 MB last-level cache, and they are launched in rotation, `rounds` times through the set
+    back to back between one pair of HIP events on `stream`, so a copy has left the cache before
+    it comes round again and the events' own overhead is spread over many launches.  Median of
+    `repeats` such runs after one untimed pass."""
     import numpy as np
+    import torch
+
+    for f in fns:
+        f()
+    ts = []
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(rounds):
+            for f in fns:
+                f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3 / (rounds * len(fns)))
+    return float(np.median(ts))
+
+
+COLD_SETS = 8   # copies of a 53.5 MB tensor in rotation: 428 MB, above the 256 MB cache
+
+
+def quantizer_rates(c, q, k, v, m, stream, rounds=3):
+    """Each quantizer and calibration kernel of the workload with its input read from HBM
+    (`cold_launch_us`: COLD_SETS copies of input and output in rotation): microseconds and GB/s
+    of algorithmic bytes (inputs read once, outputs written once).  The FP4 encoder is also timed
+    on the FP8 workloads' Q (codes + scales, and with the fused FP8 output), as the encoder of
+    the FP4 variant on the same tensor size."""
     import torch
     import precision_quantized_attention_amd as kq
 
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     n = q.numel()
     out = {}
+    qs = [q.clone() for _ in range(COLD_SETS)]
 
-    def timed(name, fn, bytes_per_elem):
-        ts = []
-        for _ in range(reps):
-            flush.fill_(1)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b) * 1e3)
-        us = float(np.median(ts))
+    def timed(name, fns, bytes_per_elem):
+        us = cold_launch_us(fns, stream, rounds=rounds)
         out[name] = {"us": round(us, 2), "gbs": round(n * bytes_per_elem / (us * 1e-6) / 1e9, 1),
                      "bytes_per_elem": round(bytes_per_elem, 4)}
 
+    def outs(shape, dtype):
+        return [torch.empty(shape, dtype=dtype, device="cuda") for _ in range(COLD_SETS)]
+
     am = torch.zeros(1, dtype=torch.float32, device="cuda")
-    timed("amax_bf16", lambda: kq.kq_amax_calibrate(q, am), 2.0)
-    s_q, inv_q = m.scales["q"]
-    q8 = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
-    timed("fp8_rows", lambda: kq.kq_quantize_fp8_tensor(q, inv_q, q8), 3.0)
-    vt = torch.empty_like(m.buf.v8t)
-    timed("fp8_transposed", lambda: kq.kq_quantize_fp8_tensor(
-        v, m.scales["v"][1], vt, layout=kq.KQ_LAYOUT_TRANSPOSED), 3.0)
+    timed("amax_bf16", [lambda x=x: kq.kq_amax_calibrate(x, am) for x in qs], 2.0)
+    inv_q = m.scales["q"][1]
+    q8 = outs(q.shape, torch.uint8)
+    timed("fp8_rows", [lambda x=x, y=y: kq.kq_quantize_fp8_tensor(x, inv_q, y)
+                       for x, y in zip(qs, q8)], 3.0)
+    vs = [v.clone() for _ in range(COLD_SETS)]
+    vt = outs(m.buf.v8t.shape, m.buf.v8t.dtype)
+    timed("fp8_transposed", [lambda x=x, y=y: kq.kq_quantize_fp8_tensor(
+        x, m.scales["v"][1], y, layout=kq.KQ_LAYOUT_TRANSPOSED) for x, y in zip(vs, vt)], 3.0)
+    del vs, vt
     d = q.shape[-1]
-    codes = torch.empty(q.shape[:-1] + (d // 2,), dtype=torch.uint8, device="cuda")
-    scales = torch.empty(q.shape[:-1] + (d // 32,), dtype=torch.uint8, device="cuda")
+    codes = outs(q.shape[:-1] + (d // 2,), torch.uint8)
+    scales = outs(q.shape[:-1] + (d // 32,), torch.uint8)
     enc = 2 + 0.5 + 1.0 / 32
-    timed("fp4_block", lambda: kq.kq_quantize_fp4_block(q, codes, scales), enc)
-    timed("fp4_block_fp8", lambda: kq.kq_quantize_fp4_block(q, codes, scales, fp8=q8,
-                                                           inv_scale8=inv_q), enc + 1)
-    dq = torch.empty_like(q)
-    timed("fp4_block_dq", lambda: kq.kq_quantize_fp4_block(q, codes, scales, dq=dq), enc + 2)
+    sets = list(zip(qs, codes, scales, q8))
+    timed("fp4_block", [lambda x=x, cd=cd, sc=sc: kq.kq_quantize_fp4_block(x, cd, sc)
+                        for x, cd, sc, _ in sets], enc)
+    timed("fp4_block_fp8", [lambda x=x, cd=cd, sc=sc, y=y: kq.kq_quantize_fp4_block(
+        x, cd, sc, fp8=y, inv_scale8=inv_q) for x, cd, sc, y in sets], enc + 1)
     if m.rope is not None:
-        timed("fp4_block_rope_fp8", lambda: kq.kq_quantize_fp4_block(
-            q, codes, scales, fp8=q8, inv_scale8=inv_q, rope=m.rope), enc + 1)
-    del flush
+        timed("fp4_block_rope_fp8", [lambda x=x, cd=cd, sc=sc, y=y: kq.kq_quantize_fp4_block(
+            x, cd, sc, fp8=y, inv_scale8=inv_q, rope=m.rope) for x, cd, sc, y in sets], enc + 1)
+    del q8
+    dq = outs(q.shape, q.dtype)
+    timed("fp4_block_dq", [lambda x=x, cd=cd, sc=sc, y=y: kq.kq_quantize_fp4_block(
+        x, cd, sc, dq=y) for (x, cd, sc, _), y in zip(sets, dq)], enc + 2)
     return out
 
 
@@ -737,9 +764,11 @@ def main():
         return
 
     if args.quantizers:
-        rates = quantizer_rates(c, q, k, v, m, stream, reps=args.steps)
-        print(json.dumps({"quantizer_kernels_cache_flushed": rates, "workload": c.name,
-                          "launches_per_kernel": args.steps, "hbm_peak_gbs": HBM_PEAK_GBS}))
+        rounds = max(1, args.steps // COLD_SETS)
+        rates = quantizer_rates(c, q, k, v, m, stream, rounds=rounds)
+        print(json.dumps({"quantizer_kernels_cold": rates, "workload": c.name,
+                          "launches_per_kernel": COLD_SETS * (1 + 5 * rounds),
+                          "hbm_peak_gbs": HBM_PEAK_GBS}))
         return
 
     ramp_steps, ramp_s = ramp(lambda: m.forward(q, k, v), args.ramp_seconds)
@@ -770,20 +799,10 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     quant_ms = float(np.mean([a.elapsed_time(b) for a, b in quant_ev]))
-    # the same with the 256 MB last-level cache flushed before every call (a 512 MB write), so
-    # the quantizers read their inputs from HBM
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = []
-    for _ in range(min(args.steps, 20)):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        m.quantize(q, k, v)
-        b.record(stream)
-        torch.cuda.synchronize()
-        cold.append(a.elapsed_time(b))
-    del flush
-    quant_cold_ms = float(np.median(cold))
+    # the same with Q, K and V read from HBM: COLD_SETS copies of them in rotation
+    cold_sets = [(q.clone(), k.clone(), v.clone()) for _ in range(COLD_SETS)]
+    quant_cold_ms = cold_launch_us([lambda t=t: m.quantize(*t) for t in cold_sets], stream) * 1e-3
+    del cold_sets
     kernels = quantizer_rates(c, q, k, v, m, stream)
 
     flops = c.flops
@@ -836,9 +855,9 @@ def main():
         "clock_ramp": {"steps": ramp_steps, "seconds": round(ramp_s, 3)},
         "quantize_ms": round(quant_ms, 4),
         "quantize_gbs": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
-        "quantize_ms_cache_flushed": round(quant_cold_ms, 4),
-        "quantize_gbs_cache_flushed": round(quant_bytes / (quant_cold_ms * 1e-3) / 1e9, 1),
-        "quantizer_kernels_cache_flushed": kernels,
+        "quantize_ms_cold": round(quant_cold_ms, 4),
+        "quantize_gbs_cold": round(quant_bytes / (quant_cold_ms * 1e-3) / 1e9, 1),
+        "quantizer_kernels_cold": kernels,
     }
     if not args.no_cpu_baseline:
         out["host_cpu"] = host_cpu()

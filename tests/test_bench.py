@@ -49,7 +49,7 @@ def test_bench_attention_line():
     assert mc["peak"] > d["roofline"]["peak"] / 2 and mc["frac"] > d["roofline"]["frac"]
     assert d["clock_ramp"]["steps"] >= 20
     for name in ("amax_bf16", "fp8_rows", "fp8_transposed", "fp4_block", "fp4_block_fp8"):
-        kd = d["quantizer_kernels_cache_flushed"][name]
+        kd = d["quantizer_kernels_cold"][name]
         assert kd["us"] > 0 and kd["gbs"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
