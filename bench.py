@@ -79,7 +79,7 @@ def parse():
                          "calls of each kernel to drop as warm-up); prints per-kernel "
                          "statistics and the kernel sources' digests")
     ap.add_argument("--pmc-summary", nargs="+", metavar=("KIND", "CSV"), default=None,
-                    help="no GPU: KIND 'traffic' or 'counters', then rocprofv3 "
+                    help="no GPU: KIND 'traffic', 'counters' or 'gemm', then rocprofv3 "
                          "counter_collection.csv files of --pmc-workload runs; prints the "
                          "summary kept under profiles/")
     return ap.parse_args()
@@ -202,7 +202,8 @@ def pmc_summary(kind, paths):
     read for the plain 1 GiB copy that opens the run (the largest __amd_rocclr_copyBuffer
     dispatch), as bytes per launch (median over dispatches).
     counters: the attention kernel's SQ/GRBM counters (medians over the dispatches past the
-    first five, whose clock is still rising) and the figures derived from them."""
+    first five, whose clock is still rising) and the figures derived from them.
+    gemm: the same for the projection GEMM kernel (a `--gemm ... --pmc-workload` run)."""
     import statistics
     vals, durs = _read_counters(paths)
     med = lambda v: statistics.median(v[5:] if len(v) > 5 else v)
@@ -221,8 +222,11 @@ def pmc_summary(kind, paths):
                     out.append(f"{name}_{tag}_bytes_per_launch: "
                                f"{round(med(vals[k][ctr]) * 1024 * sc)}")
         return "\n".join(out)
-    # counters of the attention kernel
-    k = next(n for n in vals if n.startswith("attn_fp8_kernel"))
+    # counters of the attention kernel ("counters") or of the projection GEMM ("gemm")
+    gemm = kind == "gemm"
+    k = next(n for n in vals if n.startswith("gemm_kernel" if gemm else "attn_fp8_kernel"))
+    if gemm:
+        out[0] = f"kernel_sha: {source_sha('gemm.hip')}  (gemm.hip)"
     c = {ctr: med(v) for ctr, v in vals[k].items()}
     dur_ns = statistics.median(d for (p, n), ds in durs.items() if n == k
                                for d in (ds[5:] if len(ds) > 5 else ds))
@@ -239,6 +243,15 @@ def pmc_summary(kind, paths):
     if "SQ_ACTIVE_INST_VALU" in c:
         out.append(f"valu_busy_pct: {100 * c['SQ_ACTIVE_INST_VALU'] / (cus * cyc):.1f}"
                    f"  (SQ_ACTIVE_INST_VALU / {cus} CUs / cycles)")
+    if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c:
+        out.append(f"wave_wait_pct: {100 * c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.1f}"
+                   f"  (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: waves waiting on a dependency)")
+    if gemm:
+        if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c:
+            out.append(f"lds_bank_conflict_pct: "
+                       f"{100 * c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.1f}"
+                       f"  (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)")
+        return "\n".join(out)
     if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
         out.append(f"valu_coexec_pct_of_mfma_busy: "
                    f"{100 * c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}")

@@ -11,14 +11,15 @@
 //
 // Work decomposition (CDNA4, wave64): workgroup = 8 waves (two per SIMD) = a 256 x 256 tile of
 // C; wave (wm, wn) computes 64 (m) x 128 (n) = 2 x 4 tiles of 32 x 32 on the 32x32x64 f8f6f4
-// MFMA (the scaled form for MXFP4, the unscaled one for FP8; 128 accumulator registers), with
-// a step's six operand sub-tiles read from LDS before its first MFMA.  The product is computed
-// transposed, D = B_sub · A_sub^T, so each lane owns one row m of C and stores runs of 4
-// consecutive n.  A k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements)
-// through LDS: rows padded to 80 bytes (conflict-free 16-byte operand reads), three stages so
-// a step's tile is written two steps before it is multiplied and one barrier per step
-// suffices; the HBM loads of a step are issued two steps before their LDS store (two register
-// sets), and the two waves of a SIMD hide each other's operand reads.
+// MFMA (the scaled form for MXFP4, the unscaled one for FP8; 128 accumulator registers).  The
+// product is computed transposed, D = B_sub · A_sub^T, so each lane owns one row m of C.  A
+// k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements) through LDS: rows
+// padded to 80 bytes (conflict-free 16-byte operand reads), three stages, a step's tile
+// written two steps before it is multiplied; the HBM loads of a step are issued two steps
+// before their LDS store (two register sets).  Ping-pong: the two waves of a SIMD run half a
+// step apart, one issuing its step's eight (FP8) or sixteen (FP4) MFMAs while the other
+// stages, fetches and reads its six operand sub-tiles, with a workgroup barrier between the
+// halves.  C leaves through LDS in whole 256-byte row pieces with the non-temporal hint.
 //
 // SVD-Quant in FP4 (the same section names it beside PTQ in FP8 and FP4): the weights are
 // split offline into bf16 rank-r factors and a residual in MXFP4; per forward,
@@ -78,42 +79,48 @@ __device__ __forceinline__ v8i cat8(uint4 lo, uint4 hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// One k-step of a wave's 128 (n) x 64 (m) tile: 4 sub-tiles of B rows (the MFMA's A side) and
-// 2 of A rows (its B side), each 32 bytes per lane read from the LDS stage st = [A rows][B rows]
-// codes, then [A rows][B rows] scale dwords.  FP8: lane (r, g) takes bytes 16g and 32 + 16g of
-// its row (k = 16g.., 32+16g..); FP4: k-chunk h = 0, 1 at bytes 32h + 16g (k = 64h + 32g ..),
-// with the scale byte of block 2h + g.
+// A wave's operands of one k-step, read from LDS in its memory part and consumed by its MFMAs.
 template <bool kFP4>
-__device__ __forceinline__ void kstep(v16f (&acc)[4][2], const uint8_t* st, int rbase_n,
-                                      int rbase_m, int sbase_n, int sbase_m, int g) {
+struct KOps {
   uint4 n[4][2], m[2][2];
   uint32_t sn[4], sm[2];
+};
+
+// Operand reads of one k-step of a wave's 128 (n) x 64 (m) tile: 4 sub-tiles of B rows (the
+// MFMA's A side) and 2 of A rows (its B side), each 32 bytes per lane, from the LDS stage st =
+// [A rows][B rows] codes, then [A rows][B rows] scale dwords.  FP8: lane (r, g) takes bytes 16g
+// and 32 + 16g of its row (k = 16g.., 32+16g..); FP4: k-chunk h = 0, 1 at bytes 32h + 16g
+// (k = 64h + 32g ..), with the scale byte of block 2h + g.  The empty asm uses every result,
+// so the reads have landed when it returns.
+template <bool kFP4>
+__device__ __forceinline__ void kread(KOps<kFP4>& o, const uint8_t* st, int rbase_n, int rbase_m,
+                                      int sbase_n, int sbase_m) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint8_t* pm = st + rbase_m + i * 32 * kPitch;
-    m[i][0] = *reinterpret_cast<const uint4*>(pm);
-    m[i][1] = *reinterpret_cast<const uint4*>(pm + 32);
-    if (kFP4) sm[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kOpStage + sbase_m + i * 32 * 4);
+    o.m[i][0] = *reinterpret_cast<const uint4*>(pm);
+    o.m[i][1] = *reinterpret_cast<const uint4*>(pm + 32);
+    if (kFP4) o.sm[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kOpStage + sbase_m + i * 32 * 4);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* pn = st + kOpStage + rbase_n + i * 32 * kPitch;
-    n[i][0] = *reinterpret_cast<const uint4*>(pn);
-    n[i][1] = *reinterpret_cast<const uint4*>(pn + 32);
-    if (kFP4) sn[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kOpStage + kScStage + sbase_n + i * 32 * 4);
+    o.n[i][0] = *reinterpret_cast<const uint4*>(pn);
+    o.n[i][1] = *reinterpret_cast<const uint4*>(pn + 32);
+    if (kFP4) o.sn[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kOpStage + kScStage + sbase_n + i * 32 * 4);
   }
-  // All operand reads are issued before the first MFMA (the empty asm needs every read's
-  // result): one LDS round trip per step instead of one per sub-tile pair, which the compiler
-  // would otherwise choose to save registers.
-  {
 #define KQ_V4(X_) (u32x4{(X_).x, (X_).y, (X_).z, (X_).w})
-    asm volatile("" ::"v"(KQ_V4(n[0][0])), "v"(KQ_V4(n[0][1])), "v"(KQ_V4(n[1][0])),
-                 "v"(KQ_V4(n[1][1])), "v"(KQ_V4(n[2][0])), "v"(KQ_V4(n[2][1])),
-                 "v"(KQ_V4(n[3][0])), "v"(KQ_V4(n[3][1])), "v"(KQ_V4(m[0][0])),
-                 "v"(KQ_V4(m[0][1])), "v"(KQ_V4(m[1][0])), "v"(KQ_V4(m[1][1])));
-    if (kFP4) asm volatile("" ::"v"(sn[0]), "v"(sn[1]), "v"(sn[2]), "v"(sn[3]), "v"(sm[0]), "v"(sm[1]));
+  asm volatile("" ::"v"(KQ_V4(o.n[0][0])), "v"(KQ_V4(o.n[0][1])), "v"(KQ_V4(o.n[1][0])),
+               "v"(KQ_V4(o.n[1][1])), "v"(KQ_V4(o.n[2][0])), "v"(KQ_V4(o.n[2][1])),
+               "v"(KQ_V4(o.n[3][0])), "v"(KQ_V4(o.n[3][1])), "v"(KQ_V4(o.m[0][0])),
+               "v"(KQ_V4(o.m[0][1])), "v"(KQ_V4(o.m[1][0])), "v"(KQ_V4(o.m[1][1])));
+  if (kFP4) asm volatile("" ::"v"(o.sn[0]), "v"(o.sn[1]), "v"(o.sn[2]), "v"(o.sn[3]), "v"(o.sm[0]), "v"(o.sm[1]));
 #undef KQ_V4
-  }
+}
+
+// The MFMAs of one k-step on operands kread left in registers.
+template <bool kFP4>
+__device__ __forceinline__ void kmma(v16f (&acc)[4][2], const KOps<kFP4>& o, int g) {
   if (kFP4) {
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -122,16 +129,16 @@ __device__ __forceinline__ void kstep(v16f (&acc)[4][2], const uint8_t* st, int 
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-          const int sa = (int)((sn[ni] >> (8 * (2 * h + g))) & 0xFF);
-          const int sb = (int)((sm[mi] >> (8 * (2 * h + g))) & 0xFF);
-          acc[ni][mi] = mfma<true>(cat8(n[ni][h], z), cat8(m[mi][h], z), acc[ni][mi], sa, sb);
+          const int sa = (int)((o.sn[ni] >> (8 * (2 * h + g))) & 0xFF);
+          const int sb = (int)((o.sm[mi] >> (8 * (2 * h + g))) & 0xFF);
+          acc[ni][mi] = mfma<true>(cat8(o.n[ni][h], z), cat8(o.m[mi][h], z), acc[ni][mi], sa, sb);
         }
   } else {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
-        acc[ni][mi] = mfma<false>(cat8(n[ni][0], n[ni][1]), cat8(m[mi][0], m[mi][1]),
+        acc[ni][mi] = mfma<false>(cat8(o.n[ni][0], o.n[ni][1]), cat8(o.m[mi][0], o.m[mi][1]),
                                   acc[ni][mi], 127, 127);
   }
 }
@@ -244,54 +251,106 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   KQ_LOAD(1, 1);
   KQ_STORE(1, 1);
   KQ_LOAD(2, 0);
+  KQ_FENCE();
   KQ_LOAD(3, 1);
+  KQ_FENCE();
   __syncthreads();
+  // Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 run half a step apart.  Each step of a
+  // wave is a memory part (staging, fetch, operand reads) and a matrix part (the MFMAs), each
+  // ended by a workgroup barrier, so on every SIMD one wave multiplies while the other moves
+  // data.
+  const int grp = __builtin_amdgcn_readfirstlane(w >> 2);
+  if (grp == 1) __syncthreads();
+  KOps<kFP4> ops;
   int st_mul = 0, st_wr = 2;
-  for (int s = 0; s < nsteps; s += 2) {
-    KQ_STORE(st_wr, 0);
-    KQ_LOAD(s + 4, 0);
-    KQ_FENCE();
-    kstep<kFP4>(acc, lds + st_mul * kStage, rbase_n, rbase_m, sbase_n, sbase_m, g);
-    __syncthreads();
-    st_mul = st_mul == 2 ? 0 : st_mul + 1;
-    st_wr = st_wr == 2 ? 0 : st_wr + 1;
-    if (s + 1 < nsteps) {
-      KQ_STORE(st_wr, 1);
-      KQ_LOAD(s + 5, 1);
-      KQ_FENCE();
-      kstep<kFP4>(acc, lds + st_mul * kStage, rbase_n, rbase_m, sbase_n, sbase_m, g);
-      __syncthreads();
-      st_mul = st_mul == 2 ? 0 : st_mul + 1;
-      st_wr = st_wr == 2 ? 0 : st_wr + 1;
-    }
+#define KQ_STEP(s_, R_)                                                            \
+  {                                                                               \
+    KQ_STORE(st_wr, R_);                                                          \
+    KQ_LOAD((s_) + 4, R_);                                                        \
+    kread<kFP4>(ops, lds + st_mul * kStage, rbase_n, rbase_m, sbase_n, sbase_m);   \
+    __syncthreads();                                                              \
+    __builtin_amdgcn_s_setprio(1);                                                \
+    kmma<kFP4>(acc, ops, g);                                                      \
+    __builtin_amdgcn_s_setprio(0);                                                \
+    __syncthreads();                                                              \
+    st_mul = st_mul == 2 ? 0 : st_mul + 1;                                        \
+    st_wr = st_wr == 2 ? 0 : st_wr + 1;                                           \
   }
+  // whole pairs of steps, then an odd last step: every pass of the loop ends after set 1's
+  // fetch, so the wait before set 0's store leaves set 1's fetch in flight
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    KQ_STEP(s, 0);
+    KQ_STEP(s + 1, 1);
+  }
+  if (s < nsteps) KQ_STEP(s, 0);
+#undef KQ_STEP
+  if (grp == 0) __syncthreads();
 #undef KQ_LOAD
 #undef KQ_STORE
 
   // epilogue: lane (r, g) owns row m = mt*256 + wm*64 + 32 mi + r and, for each sub-tile ni,
-  // columns n = nt*256 + wn*128 + 32 ni + 8q + 4g .. +3 (q = 0..3): a float4, or 4 bf16
+  // columns n = nt*256 + wn*128 + 32 ni + 8q + 4g .. +3 (q = 0..3).  The wave's 64 x 128 tile
+  // leaves through the wave's own 8 KB of the (now idle) stages, 32 rows by 256 bytes at a
+  // time (float32: 64 columns, sub-tiles 2h and 2h + 1; bf16: all 128), so every store
+  // instruction writes whole 256-byte row pieces, with the non-temporal hint: the 64 MB a
+  // round of tiles writes would otherwise evict the next round's A and B tiles from the L2.
+  // LDS row rr holds its 16-byte granule j at j ^ (rr & 15).
+  __syncthreads();
   const float scale = p.scale;
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  uint8_t* wl = lds + w * 8192;
+  constexpr int kPieces = kBf16 ? 1 : 2;       // 256-byte pieces of a row of the wave's tile
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
-    const int m = mt * kTile + wm * 64 + 32 * mi + r;
-    if (m >= p.m) continue;
+    const int m0 = mt * kTile + wm * 64 + 32 * mi;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int h = 0; h < kPieces; ++h) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nt * kTile + wn * 128 + 32 * ni + 8 * q + 4 * g;
-        if (n < p.n) {
+      for (int nj = 0; nj < 4 / kPieces; ++nj) {
+        const int ni = (4 / kPieces) * h + nj;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
           const v16f& c = acc[ni][mi];
           const float c0 = c[4 * q] * scale, c1 = c[4 * q + 1] * scale;
           const float c2 = c[4 * q + 2] * scale, c3 = c[4 * q + 3] * scale;
-          const int64_t off = (int64_t)m * p.n + n;
-          if constexpr (kBf16)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.c) + off) =
+          if constexpr (kBf16) {
+            const int j = 4 * ni + q;                 // columns 8j .. 8j + 7
+            *reinterpret_cast<uint2*>(wl + r * 256 + 16 * (j ^ (r & 15)) + 8 * g) =
                 make_uint2(bf16x2_rne(c0, c1), bf16x2_rne(c2, c3));
-          else
-            *reinterpret_cast<float4*>(static_cast<float*>(p.c) + off) = make_float4(c0, c1, c2, c3);
+          } else {
+            const int j = 8 * nj + 2 * q + g;         // columns 64h + 4j .. + 3
+            *reinterpret_cast<float4*>(wl + r * 256 + 16 * (j ^ (r & 15))) = make_float4(c0, c1, c2, c3);
+          }
         }
       }
+      // 4 rows of 16 granules per instruction
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = 4 * i + (l >> 4), j = l & 15;
+        const u4v v = *reinterpret_cast<const u4v*>(wl + rr * 256 + 16 * (j ^ (rr & 15)));
+        const int m = m0 + rr;
+        if (m >= p.m) continue;
+        if constexpr (kBf16) {
+          const int n = nt * kTile + wn * 128 + 8 * j;
+          uint16_t* dst = static_cast<uint16_t*>(p.c) + (int64_t)m * p.n + n;
+          if (n < p.n) {
+            if ((p.n & 7) == 0) {
+              __builtin_nontemporal_store(v, reinterpret_cast<u4v*>(dst));
+            } else {
+              // N % 8 == 4: rows start 8-byte aligned only; 4 columns per store
+              typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+              __builtin_nontemporal_store(u2v{v[0], v[1]}, reinterpret_cast<u2v*>(dst));
+              if (n + 4 < p.n) __builtin_nontemporal_store(u2v{v[2], v[3]}, reinterpret_cast<u2v*>(dst + 4));
+            }
+          }
+        } else {
+          const int n = nt * kTile + wn * 128 + 64 * h + 4 * j;
+          if (n < p.n)
+            __builtin_nontemporal_store(v, reinterpret_cast<u4v*>(static_cast<float*>(p.c) + (int64_t)m * p.n + n));
+        }
+      }
+    }
   }
 }
 
