@@ -16,7 +16,8 @@
 // k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements) through LDS: rows
 // padded to 80 bytes (conflict-free 16-byte operand reads), three stages, a step's tile
 // written two steps before it is multiplied; the HBM loads of a step are issued two steps
-// before their LDS store (two register sets).  Ping-pong: the two waves of a SIMD run half a
+// before their LDS store (two register sets); MXFP4 scales go through a two-slot LDS ring,
+// fetched 16 bytes (four k-steps) per row at a time.  Ping-pong: the two waves of a SIMD run half a
 // step apart, one issuing its step's eight (FP8) or sixteen (FP4) MFMAs while the other
 // stages, fetches and reads its six operand sub-tiles, with a workgroup barrier between the
 // halves.  C leaves through LDS in whole 256-byte row pieces with the non-temporal hint.
@@ -48,9 +49,12 @@ constexpr int kThreads = 512;         // 8 waves, two per SIMD
 constexpr int kRowBytes = 64;         // bytes of one operand row per k-step
 constexpr int kPitch = kRowBytes + 16;
 constexpr int kOpStage = kTile * kPitch;            // 20480 bytes per operand
-constexpr int kScStage = kTile * 4;                 // 4 E8M0 bytes per row per k-step (FP4)
-constexpr int kStage = 2 * kOpStage + 2 * kScStage; // A, B codes + A, B scales
+constexpr int kStage = 2 * kOpStage;                // A, B codes
 constexpr int kStages = 3;
+// FP4 scales: a ring of two slots, each 4 k-steps of the 512 operand rows' E8M0 dwords
+// (row rho: 16 bytes at rho * 16, dword = k-step mod 4)
+constexpr int kRingSlot = 2 * kTile * 16;
+constexpr int kRing = 2 * kRingSlot;
 constexpr int kGroupM = 8;            // tiles of M visited together (L2 reuse of B tiles)
 
 #define KQ_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -93,21 +97,21 @@ struct KOps {
 // (k = 64h + 32g ..), with the scale byte of block 2h + g.  The empty asm uses every result,
 // so the reads have landed when it returns.
 template <bool kFP4>
-__device__ __forceinline__ void kread(KOps<kFP4>& o, const uint8_t* st, int rbase_n, int rbase_m,
-                                      int sbase_n, int sbase_m) {
+__device__ __forceinline__ void kread(KOps<kFP4>& o, const uint8_t* st, const uint8_t* sc,
+                                      int rbase_n, int rbase_m, int sbase_n, int sbase_m) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint8_t* pm = st + rbase_m + i * 32 * kPitch;
     o.m[i][0] = *reinterpret_cast<const uint4*>(pm);
     o.m[i][1] = *reinterpret_cast<const uint4*>(pm + 32);
-    if (kFP4) o.sm[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kOpStage + sbase_m + i * 32 * 4);
+    if (kFP4) o.sm[i] = *reinterpret_cast<const uint32_t*>(sc + sbase_m + i * 32 * 16);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* pn = st + kOpStage + rbase_n + i * 32 * kPitch;
     o.n[i][0] = *reinterpret_cast<const uint4*>(pn);
     o.n[i][1] = *reinterpret_cast<const uint4*>(pn + 32);
-    if (kFP4) o.sn[i] = *reinterpret_cast<const uint32_t*>(st + 2 * kOpStage + kScStage + sbase_n + i * 32 * 4);
+    if (kFP4) o.sn[i] = *reinterpret_cast<const uint32_t*>(sc + sbase_n + i * 32 * 16);
   }
 #define KQ_V4(X_) (u32x4{(X_).x, (X_).y, (X_).z, (X_).w})
   asm volatile("" ::"v"(KQ_V4(o.n[0][0])), "v"(KQ_V4(o.n[0][1])), "v"(KQ_V4(o.n[1][0])),
@@ -151,7 +155,8 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 
 template <bool kFP4, bool kBf16, bool kLowRank>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStage + (kFP4 ? kRing : 0)];
+  uint8_t* const ring = lds + kStages * kStage;
   const int tiles_m = (p.m + kTile - 1) / kTile, tiles_n = (p.n + kTile - 1) / kTile;
   const int total = tiles_m * tiles_n;
   // XCD-aware order: each XCD takes a contiguous range of tiles, visited in groups of kGroupM
@@ -175,8 +180,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t br = make_rsrc(p.b, (uint32_t)p.n * row_bytes);
 
   // staging: each operand tile is 256 rows x 4 chunks of 16 bytes; thread t owns chunks t and
-  // t + 512 of both (rows t/4 and t/4 + 128, chunk t % 4); for FP4, threads 0-255 stage the
-  // scale dword of A row t and threads 256-511 that of B row t - 256
+  // t + 512 of both (rows t/4 and t/4 + 128, chunk t % 4).  FP4 scales: thread t owns the E8M0
+  // dwords of operand row t (A rows 0-255, then B rows), fetched 16 bytes (4 k-steps) at a
+  // time four steps ahead and written to the ring slot of their block; one dword per row per
+  // step would touch a 128-byte line for 4 useful bytes, every step.
   const int crow = tid >> 2, cchunk = tid & 3;
   const uint32_t goff_a = (uint32_t)(mt * kTile + crow) * row_bytes + 16 * cchunk;
   const uint32_t goff_b = (uint32_t)(nt * kTile + crow) * row_bytes + 16 * cchunk;
@@ -186,10 +193,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t scr =
       make_rsrc(sc_a ? p.a_scales : p.b_scales, (uint32_t)(sc_a ? p.m : p.n) * sc_bytes);
   const uint32_t soff = (uint32_t)((sc_a ? mt : nt) * kTile + (tid & 255)) * sc_bytes;
-  const int sloff = 2 * kOpStage + (sc_a ? 0 : kScStage) + 4 * (tid & 255);
+  // the 16 bytes of scale block c (k-steps 4c .. 4c+3) of this thread's row; rows whose scale
+  // bytes are not a multiple of 16 take four dword loads
+  const bool sc_al = (sc_bytes & 15) == 0;
+  auto sload = [&](int c) -> uint4 {
+    const uint32_t o_ = soff + 16u * (uint32_t)c;
+    if (sc_al) return bload16(scr, o_);
+    return make_uint4(bload4(scr, o_), bload4(scr, o_ + 4), bload4(scr, o_ + 8), bload4(scr, o_ + 12));
+  };
 
   uint4 xa0[2], xa1[2], xb0[2], xb1[2];
-  uint32_t xs[2] = {0, 0};
 #define KQ_LOAD(s, R)                                                     \
   {                                                                       \
     const uint32_t o_ = (uint32_t)(s) * kRowBytes;                        \
@@ -197,7 +210,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     xa1[R] = bload16(ar, goff_a + row128 + o_);                           \
     xb0[R] = bload16(br, goff_b + o_);                                    \
     xb1[R] = bload16(br, goff_b + row128 + o_);                           \
-    if (kFP4) xs[R] = bload4(scr, soff + 4 * (uint32_t)(s));              \
   }
 #define KQ_STORE(stage, R)                                                \
   {                                                                       \
@@ -206,12 +218,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     *reinterpret_cast<uint4*>(st_ + loff + 128 * kPitch) = xa1[R];        \
     *reinterpret_cast<uint4*>(st_ + kOpStage + loff) = xb0[R];            \
     *reinterpret_cast<uint4*>(st_ + kOpStage + loff + 128 * kPitch) = xb1[R]; \
-    if (kFP4) *reinterpret_cast<uint32_t*>(st_ + sloff) = xs[R];          \
   }
 
   const int rbase_n = (wn * 128 + r) * kPitch + 16 * g;
   const int rbase_m = (wm * 64 + r) * kPitch + 16 * g;
-  const int sbase_n = (wn * 128 + r) * 4, sbase_m = (wm * 64 + r) * 4;
+  const int sbase_n = (kTile + wn * 128 + r) * 16, sbase_m = (wm * 64 + r) * 16;
 
   v16f acc[4][2];
 #pragma unroll
@@ -246,6 +257,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   // (read last in step s - 1), fetches step s + 4 into the same set and multiplies stage s % 3
   // (stored in step s - 2).  Past the last step the fetches read bytes of the next rows (or
   // zeros past the end) into stages nothing reads.
+  uint4 xq = make_uint4(0, 0, 0, 0);     // FP4: scale block of the next ring write
+  if constexpr (kFP4) {
+    *reinterpret_cast<uint4*>(ring + 16 * tid) = sload(0);
+    xq = sload(1);
+  }
   KQ_LOAD(0, 0);
   KQ_STORE(0, 0);
   KQ_LOAD(1, 1);
@@ -263,11 +279,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   if (grp == 1) __syncthreads();
   KOps<kFP4> ops;
   int st_mul = 0, st_wr = 2;
-#define KQ_STEP(s_, R_)                                                            \
+#define KQ_STEP(s_, R_, RING_)                                                     \
   {                                                                               \
+    if (kFP4 && (RING_)) {                                                        \
+      /* scale block (s_)/4 + 1 into its slot (read last in step (s_) - 1), then   \
+         fetch block (s_)/4 + 2 */                                                \
+      *reinterpret_cast<uint4*>(ring + ((((s_) >> 2) + 1) & 1) * kRingSlot + 16 * tid) = xq; \
+      xq = sload(((s_) >> 2) + 2);                                                \
+    }                                                                             \
     KQ_STORE(st_wr, R_);                                                          \
     KQ_LOAD((s_) + 4, R_);                                                        \
-    kread<kFP4>(ops, lds + st_mul * kStage, rbase_n, rbase_m, sbase_n, sbase_m);   \
+    kread<kFP4>(ops, lds + st_mul * kStage,                                       \
+                ring + (((s_) >> 2) & 1) * kRingSlot + 4 * ((s_) & 3),            \
+                rbase_n, rbase_m, sbase_n, sbase_m);                              \
     __syncthreads();                                                              \
     __builtin_amdgcn_s_setprio(1);                                                \
     kmma<kFP4>(acc, ops, g);                                                      \
@@ -276,14 +300,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     st_mul = st_mul == 2 ? 0 : st_mul + 1;                                        \
     st_wr = st_wr == 2 ? 0 : st_wr + 1;                                           \
   }
-  // whole pairs of steps, then an odd last step: every pass of the loop ends after set 1's
-  // fetch, so the wait before set 0's store leaves set 1's fetch in flight
+  // blocks of four steps (a ring write at the first), then up to three more
   int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    KQ_STEP(s, 0);
-    KQ_STEP(s + 1, 1);
+  for (; s + 3 < nsteps; s += 4) {
+    KQ_STEP(s, 0, true);
+    KQ_STEP(s + 1, 1, false);
+    KQ_STEP(s + 2, 0, false);
+    KQ_STEP(s + 3, 1, false);
   }
-  if (s < nsteps) KQ_STEP(s, 0);
+  if (s < nsteps) KQ_STEP(s, 0, true);
+  if (s + 1 < nsteps) KQ_STEP(s + 1, 1, false);
+  if (s + 2 < nsteps) KQ_STEP(s + 2, 0, false);
 #undef KQ_STEP
   if (grp == 0) __syncthreads();
 #undef KQ_LOAD
