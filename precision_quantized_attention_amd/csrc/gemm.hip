@@ -17,7 +17,8 @@
 // padded to 80 bytes (conflict-free 16-byte operand reads), three stages, a step's tile
 // written two steps before it is multiplied; the HBM loads of a step are issued two steps
 // before their LDS store (two register sets); MXFP4 scales go through a two-slot LDS ring,
-// fetched 16 bytes (four k-steps) per row at a time.  Ping-pong: the two waves of a SIMD run half a
+// fetched 16 bytes (four k-steps) per row at a time and read once per two steps, the MFMA's
+// scale select picking each step's byte.  Ping-pong: the two waves of a SIMD run half a
 // step apart, one issuing its step's eight (FP8) or sixteen (FP4) MFMAs while the other
 // stages, fetches and reads its six operand sub-tiles, with a workgroup barrier between the
 // halves.  C leaves through LDS in whole 256-byte row pieces with the non-temporal hint.
@@ -51,8 +52,14 @@ constexpr int kPitch = kRowBytes + 16;
 constexpr int kOpStage = kTile * kPitch;            // 20480 bytes per operand
 constexpr int kStage = 2 * kOpStage;                // A, B codes
 constexpr int kStages = 3;
-// FP4 scales: a ring of two slots, each 4 k-steps of the 512 operand rows' E8M0 dwords
-// (row rho: 16 bytes at rho * 16, dword = k-step mod 4)
+// FP4 scales: a ring of two slots, each holding 4 k-steps of the 512 operand rows' E8M0 bytes.
+// Dword j = 2p + g of a row holds blocks g and 2 + g of k-step 2p (bytes 0, 1) and of k-step
+// 2p + 1 (bytes 2, 3) of the slot's four steps: what lane group g of a 32-row sub-tile needs for
+// the step pair p.  A slot stores the dwords of one j contiguously per lane: A row
+// m = 64 wm + 32 i + r at ((j * 128 + 32 wm + r) * 2 + i) * 4 (a lane's two A rows in 8 bytes),
+// B row n = 128 wn + 32 i + r at 4096 + ((j * 64 + 32 wn + r) * 4 + i) * 4 (its four B rows in
+// 16 bytes), so the reads of a step pair are one 8- and one 16-byte read per lane, and a wave's
+// reads fall on consecutive addresses (no bank conflicts).
 constexpr int kRingSlot = 2 * kTile * 16;
 constexpr int kRing = 2 * kRingSlot;
 constexpr int kGroupM = 8;            // tiles of M visited together (L2 reuse of B tiles)
@@ -73,9 +80,7 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 // A wave holds 8 tiles of 32 x 32 (128 accumulator registers) and two waves share each SIMD.
 // FP8 takes the unscaled form (zero scale operands select v_mfma_f32_32x32x64_f8f6f4).
-template <bool kFP4>
-__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c, int sa, int sb) {
-  if (kFP4) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+__device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
@@ -92,11 +97,12 @@ struct KOps {
 
 // Operand reads of one k-step of a wave's 128 (n) x 64 (m) tile: 4 sub-tiles of B rows (the
 // MFMA's A side) and 2 of A rows (its B side), each 32 bytes per lane, from the LDS stage st =
-// [A rows][B rows] codes, then [A rows][B rows] scale dwords.  FP8: lane (r, g) takes bytes 16g
-// and 32 + 16g of its row (k = 16g.., 32+16g..); FP4: k-chunk h = 0, 1 at bytes 32h + 16g
-// (k = 64h + 32g ..), with the scale byte of block 2h + g.  The empty asm uses every result,
-// so the reads have landed when it returns.
-template <bool kFP4>
+// [A rows][B rows] codes.  FP8: lane (r, g) takes bytes 16g and 32 + 16g of its row
+// (k = 16g.., 32+16g..); FP4: k-chunk h = 0, 1 at bytes 32h + 16g (k = 64h + 32g ..).  FP4 with
+// kSc (the first step of a pair) also reads the lane's scale dwords of the pair from the ring
+// slot sc; the second step keeps them.  The empty asm uses every result, so the reads have
+// landed when it returns.
+template <bool kFP4, bool kSc>
 __device__ __forceinline__ void kread(KOps<kFP4>& o, const uint8_t* st, const uint8_t* sc,
                                       int rbase_n, int rbase_m, int sbase_n, int sbase_m) {
 #pragma unroll
@@ -104,46 +110,72 @@ __device__ __forceinline__ void kread(KOps<kFP4>& o, const uint8_t* st, const ui
     const uint8_t* pm = st + rbase_m + i * 32 * kPitch;
     o.m[i][0] = *reinterpret_cast<const uint4*>(pm);
     o.m[i][1] = *reinterpret_cast<const uint4*>(pm + 32);
-    if (kFP4) o.sm[i] = *reinterpret_cast<const uint32_t*>(sc + sbase_m + i * 32 * 16);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint8_t* pn = st + kOpStage + rbase_n + i * 32 * kPitch;
     o.n[i][0] = *reinterpret_cast<const uint4*>(pn);
     o.n[i][1] = *reinterpret_cast<const uint4*>(pn + 32);
-    if (kFP4) o.sn[i] = *reinterpret_cast<const uint32_t*>(sc + sbase_n + i * 32 * 16);
+  }
+  if (kFP4 && kSc) {
+    const uint2 mv = *reinterpret_cast<const uint2*>(sc + sbase_m);
+    const uint4 nv = *reinterpret_cast<const uint4*>(sc + sbase_n);
+    o.sm[0] = mv.x; o.sm[1] = mv.y;
+    o.sn[0] = nv.x; o.sn[1] = nv.y; o.sn[2] = nv.z; o.sn[3] = nv.w;
   }
 #define KQ_V4(X_) (u32x4{(X_).x, (X_).y, (X_).z, (X_).w})
   asm volatile("" ::"v"(KQ_V4(o.n[0][0])), "v"(KQ_V4(o.n[0][1])), "v"(KQ_V4(o.n[1][0])),
                "v"(KQ_V4(o.n[1][1])), "v"(KQ_V4(o.n[2][0])), "v"(KQ_V4(o.n[2][1])),
                "v"(KQ_V4(o.n[3][0])), "v"(KQ_V4(o.n[3][1])), "v"(KQ_V4(o.m[0][0])),
                "v"(KQ_V4(o.m[0][1])), "v"(KQ_V4(o.m[1][0])), "v"(KQ_V4(o.m[1][1])));
-  if (kFP4) asm volatile("" ::"v"(o.sn[0]), "v"(o.sn[1]), "v"(o.sn[2]), "v"(o.sn[3]), "v"(o.sm[0]), "v"(o.sm[1]));
+  if (kFP4 && kSc) asm volatile("" ::"v"(o.sn[0]), "v"(o.sn[1]), "v"(o.sn[2]), "v"(o.sn[3]), "v"(o.sm[0]), "v"(o.sm[1]));
 #undef KQ_V4
 }
 
-// The MFMAs of one k-step on operands kread left in registers.
-template <bool kFP4>
-__device__ __forceinline__ void kmma(v16f (&acc)[4][2], const KOps<kFP4>& o, int g) {
-  if (kFP4) {
-    const uint4 z = make_uint4(0, 0, 0, 0);
+// E8M0 bytes of four k-steps of a row (dword c = step c, byte i = block i) in the ring's order:
+// dword 2p + g = blocks g and 2 + g of step 2p, then of step 2p + 1.
+__device__ __forceinline__ uint4 ring_order(uint4 x) {
+  auto pick = [](uint32_t a, uint32_t b, int g) -> uint32_t {
+    return ((a >> (8 * g)) & 0xFFu) | (((a >> (8 * g + 16)) & 0xFFu) << 8) |
+           (((b >> (8 * g)) & 0xFFu) << 16) | (((b >> (8 * g + 16)) & 0xFFu) << 24);
+  };
+  return make_uint4(pick(x.x, x.y, 0), pick(x.x, x.y, 1), pick(x.z, x.w, 0), pick(x.z, x.w, 1));
+}
+
+// A row's four ring dwords (j = 0..3) at p + 1024 j.
+__device__ __forceinline__ void ring_put(uint8_t* p, uint4 v) {
+  *reinterpret_cast<uint32_t*>(p) = v.x;
+  *reinterpret_cast<uint32_t*>(p + 1024) = v.y;
+  *reinterpret_cast<uint32_t*>(p + 2048) = v.z;
+  *reinterpret_cast<uint32_t*>(p + 3072) = v.w;
+}
+
+// FP4 MFMAs of k-chunk h: the scale select kSel picks byte kSel of each scale dword (the block
+// of chunk h of this step; see the ring layout), so no instruction extracts it.
+template <int kSel>
+__device__ __forceinline__ void kmma_fp4_chunk(v16f (&acc)[4][2], const KOps<true>& o, int h) {
+  const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const int sa = (int)((o.sn[ni] >> (8 * (2 * h + g))) & 0xFF);
-          const int sb = (int)((o.sm[mi] >> (8 * (2 * h + g))) & 0xFF);
-          acc[ni][mi] = mfma<true>(cat8(o.n[ni][h], z), cat8(o.m[mi][h], z), acc[ni][mi], sa, sb);
-        }
+    for (int mi = 0; mi < 2; ++mi)
+      acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          cat8(o.n[ni][h], z), cat8(o.m[mi][h], z), acc[ni][mi], 4, 4, kSel, (int)o.sn[ni], kSel,
+          (int)o.sm[mi]);
+}
+
+// The MFMAs of one k-step on operands kread left in registers; kPar is the step's parity.
+template <bool kFP4, int kPar>
+__device__ __forceinline__ void kmma(v16f (&acc)[4][2], const KOps<kFP4>& o) {
+  if constexpr (kFP4) {
+    kmma_fp4_chunk<2 * kPar>(acc, o, 0);
+    kmma_fp4_chunk<2 * kPar + 1>(acc, o, 1);
   } else {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
-        acc[ni][mi] = mfma<false>(cat8(o.n[ni][0], o.n[ni][1]), cat8(o.m[mi][0], o.m[mi][1]),
-                                  acc[ni][mi], 127, 127);
+        acc[ni][mi] = mfma_fp8(cat8(o.n[ni][0], o.n[ni][1]), cat8(o.m[mi][0], o.m[mi][1]), acc[ni][mi]);
   }
 }
 
@@ -181,7 +213,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 
   // staging: each operand tile is 256 rows x 4 chunks of 16 bytes; thread t owns chunks t and
   // t + 512 of both (rows t/4 and t/4 + 128, chunk t % 4).  FP4 scales: thread t owns the E8M0
-  // dwords of operand row t (A rows 0-255, then B rows), fetched 16 bytes (4 k-steps) at a
+  // bytes of operand row t (A rows 0-255, then B rows), fetched 16 bytes (4 k-steps) at a
   // time four steps ahead and written to the ring slot of their block; one dword per row per
   // step would touch a 128-byte line for 4 useful bytes, every step.
   const int crow = tid >> 2, cchunk = tid & 3;
@@ -222,7 +254,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 
   const int rbase_n = (wn * 128 + r) * kPitch + 16 * g;
   const int rbase_m = (wm * 64 + r) * kPitch + 16 * g;
-  const int sbase_n = (kTile + wn * 128 + r) * 16, sbase_m = (wm * 64 + r) * 16;
+  // ring reads of lane (r, g) (j = 2p + g for step pair p) and this thread's ring row
+  const int sbase_n = 4096 + (g * 64 + wn * 32 + r) * 16, sbase_m = (g * 128 + wm * 32 + r) * 8;
+  const int wbase = tid < kTile ? (((tid >> 6) * 32 + (tid & 31)) * 2 + ((tid >> 5) & 1)) * 4
+                                : 4096 + ((((tid - kTile) >> 7) * 32 + (tid & 31)) * 4 + ((tid >> 5) & 3)) * 4;
 
   v16f acc[4][2];
 #pragma unroll
@@ -259,7 +294,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   // zeros past the end) into stages nothing reads.
   uint4 xq = make_uint4(0, 0, 0, 0);     // FP4: scale block of the next ring write
   if constexpr (kFP4) {
-    *reinterpret_cast<uint4*>(ring + 16 * tid) = sload(0);
+    ring_put(ring + wbase, ring_order(sload(0)));
     xq = sload(1);
   }
   KQ_LOAD(0, 0);
@@ -279,22 +314,24 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   if (grp == 1) __syncthreads();
   KOps<kFP4> ops;
   int st_mul = 0, st_wr = 2;
+  // KQ_STEP(s, R, RING): R = s mod 2 (the fetch register set, and the step's parity within its
+  // scale pair), RING = (s mod 4 == 0)
 #define KQ_STEP(s_, R_, RING_)                                                     \
   {                                                                               \
     if (kFP4 && (RING_)) {                                                        \
       /* scale block (s_)/4 + 1 into its slot (read last in step (s_) - 1), then   \
          fetch block (s_)/4 + 2 */                                                \
-      *reinterpret_cast<uint4*>(ring + ((((s_) >> 2) + 1) & 1) * kRingSlot + 16 * tid) = xq; \
+      ring_put(ring + ((((s_) >> 2) + 1) & 1) * kRingSlot + wbase, ring_order(xq)); \
       xq = sload(((s_) >> 2) + 2);                                                \
     }                                                                             \
     KQ_STORE(st_wr, R_);                                                          \
     KQ_LOAD((s_) + 4, R_);                                                        \
-    kread<kFP4>(ops, lds + st_mul * kStage,                                       \
-                ring + (((s_) >> 2) & 1) * kRingSlot + 4 * ((s_) & 3),            \
+    kread<kFP4, (R_) == 0>(ops, lds + st_mul * kStage,                            \
+                ring + (((s_) >> 2) & 1) * kRingSlot + 2048 * (((s_) >> 1) & 1),  \
                 rbase_n, rbase_m, sbase_n, sbase_m);                              \
     __syncthreads();                                                              \
     __builtin_amdgcn_s_setprio(1);                                                \
-    kmma<kFP4>(acc, ops, g);                                                      \
+    kmma<kFP4, (R_)>(acc, ops);                                                   \
     __builtin_amdgcn_s_setprio(0);                                                \
     __syncthreads();                                                              \
     st_mul = st_mul == 2 ? 0 : st_mul + 1;                                        \
