@@ -13,8 +13,9 @@
 // C; wave (wm, wn) computes 64 (m) x 128 (n) = 2 x 4 tiles of 32 x 32 on the 32x32x64 f8f6f4
 // MFMA (the scaled form for MXFP4, the unscaled one for FP8; 128 accumulator registers).  The
 // product is computed transposed, D = B_sub · A_sub^T, so each lane owns one row m of C.  A
-// k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements) through LDS: rows
-// padded to 80 bytes (conflict-free 16-byte operand reads), three stages, a step's tile
+// k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements) through LDS: 64-byte
+// rows with the 16-byte chunks swizzled (conflict-free staging writes and operand reads), three
+// stages, a step's tile
 // written two steps before it is multiplied; the HBM loads of a step are issued two steps
 // before their LDS store (two register sets); MXFP4 scales go through a two-slot LDS ring,
 // fetched 16 bytes (four k-steps) per row at a time and read once per two steps, the MFMA's
@@ -48,8 +49,11 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kTile = 256;            // workgroup tile of C (M and N)
 constexpr int kThreads = 512;         // 8 waves, two per SIMD
 constexpr int kRowBytes = 64;         // bytes of one operand row per k-step
-constexpr int kPitch = kRowBytes + 16;
-constexpr int kOpStage = kTile * kPitch;            // 20480 bytes per operand
+// LDS stage rows: chunk c (16 bytes) of row R at 16 * (c ^ ((R >> 2) & 3)).  A staging store
+// instruction covers rows 4q .. 4q+3 x chunks 0-3 in each 16-lane group and an operand read 16
+// consecutive rows x one chunk; with the swizzle both touch 16 distinct 16-byte bank groups.
+constexpr int kPitch = kRowBytes;
+constexpr int kOpStage = kTile * kPitch;            // 16384 bytes per operand
 constexpr int kStage = 2 * kOpStage;                // A, B codes
 constexpr int kStages = 3;
 // FP4 scales: a ring of two slots, each holding 4 k-steps of the 512 operand rows' E8M0 bytes.
@@ -104,18 +108,17 @@ struct KOps {
 // landed when it returns.
 template <bool kFP4, bool kSc>
 __device__ __forceinline__ void kread(KOps<kFP4>& o, const uint8_t* st, const uint8_t* sc,
-                                      int rbase_n, int rbase_m, int sbase_n, int sbase_m) {
+                                      int rbase_n, int rbase_m, int rbase_n2, int rbase_m2,
+                                      int sbase_n, int sbase_m) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const uint8_t* pm = st + rbase_m + i * 32 * kPitch;
-    o.m[i][0] = *reinterpret_cast<const uint4*>(pm);
-    o.m[i][1] = *reinterpret_cast<const uint4*>(pm + 32);
+    o.m[i][0] = *reinterpret_cast<const uint4*>(st + rbase_m + i * 32 * kPitch);
+    o.m[i][1] = *reinterpret_cast<const uint4*>(st + rbase_m2 + i * 32 * kPitch);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint8_t* pn = st + kOpStage + rbase_n + i * 32 * kPitch;
-    o.n[i][0] = *reinterpret_cast<const uint4*>(pn);
-    o.n[i][1] = *reinterpret_cast<const uint4*>(pn + 32);
+    o.n[i][0] = *reinterpret_cast<const uint4*>(st + kOpStage + rbase_n + i * 32 * kPitch);
+    o.n[i][1] = *reinterpret_cast<const uint4*>(st + kOpStage + rbase_n2 + i * 32 * kPitch);
   }
   if (kFP4 && kSc) {
     const uint2 mv = *reinterpret_cast<const uint2*>(sc + sbase_m);
@@ -220,7 +223,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const uint32_t goff_a = (uint32_t)(mt * kTile + crow) * row_bytes + 16 * cchunk;
   const uint32_t goff_b = (uint32_t)(nt * kTile + crow) * row_bytes + 16 * cchunk;
   const uint32_t row128 = 128u * row_bytes;
-  const int loff = crow * kPitch + 16 * cchunk;
+  const int loff = crow * kPitch + 16 * (cchunk ^ ((crow >> 2) & 3));   // rows crow and crow + 128
   const bool sc_a = __builtin_amdgcn_readfirstlane(tid) < 256;
   const __amdgpu_buffer_rsrc_t scr =
       make_rsrc(sc_a ? p.a_scales : p.b_scales, (uint32_t)(sc_a ? p.m : p.n) * sc_bytes);
@@ -252,8 +255,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     *reinterpret_cast<uint4*>(st_ + kOpStage + loff + 128 * kPitch) = xb1[R]; \
   }
 
-  const int rbase_n = (wn * 128 + r) * kPitch + 16 * g;
-  const int rbase_m = (wm * 64 + r) * kPitch + 16 * g;
+  // operand reads of lane (r, g): chunks g and g + 2 of its rows (sub-tile rows are 32 apart,
+  // so every row of the lane has the swizzle of r)
+  const int cx = g ^ ((r >> 2) & 3);
+  const int rbase_n = (wn * 128 + r) * kPitch + 16 * cx, rbase_n2 = (wn * 128 + r) * kPitch + 16 * (cx ^ 2);
+  const int rbase_m = (wm * 64 + r) * kPitch + 16 * cx, rbase_m2 = (wm * 64 + r) * kPitch + 16 * (cx ^ 2);
   // ring reads of lane (r, g) (j = 2p + g for step pair p) and this thread's ring row
   const int sbase_n = 4096 + (g * 64 + wn * 32 + r) * 16, sbase_m = (g * 128 + wm * 32 + r) * 8;
   const int wbase = tid < kTile ? (((tid >> 6) * 32 + (tid & 31)) * 2 + ((tid >> 5) & 1)) * 4
@@ -319,7 +325,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 #define KQ_STEP(s_, R_, RING_)                                                     \
   {                                                                               \
     if (kFP4 && (RING_)) {                                                        \
-      /* scale block (s_)/4 + 1 into its slot (read last in step (s_) - 1), then   \
+      /* scale block (s_)/4 + 1 into its slot (read last in step (s_) - 2), then   \
          fetch block (s_)/4 + 2 */                                                \
       ring_put(ring + ((((s_) >> 2) + 1) & 1) * kRingSlot + wbase, ring_order(xq)); \
       xq = sload(((s_) >> 2) + 2);                                                \
@@ -328,7 +334,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     KQ_LOAD((s_) + 4, R_);                                                        \
     kread<kFP4, (R_) == 0>(ops, lds + st_mul * kStage,                            \
                 ring + (((s_) >> 2) & 1) * kRingSlot + 2048 * (((s_) >> 1) & 1),  \
-                rbase_n, rbase_m, sbase_n, sbase_m);                              \
+                rbase_n, rbase_m, rbase_n2, rbase_m2, sbase_n, sbase_m);          \
     __syncthreads();                                                              \
     __builtin_amdgcn_s_setprio(1);                                                \
     kmma<kFP4, (R_)>(acc, ops);                                                   \
