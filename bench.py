@@ -789,13 +789,14 @@ def main():
         m.forward(q, k, v)
     torch.cuda.synchronize()
 
-    # timed steps (forward = quantize, then attention); HIP events on the attention's stream
-    # bracket its launch inside each timed step
+    # timed steps (forward = the per-forward quantization, then attention; in FP8 mode K and V
+    # through the quantizers and Q inside the attention kernel); HIP events on the attention's
+    # stream bracket its launch inside each timed step
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in ev:
-        m.quantize(q, k, v)
+        m.prepare(q, k, v)
         a.record(stream)
         m.attention()
         b.record(stream)
@@ -808,13 +809,13 @@ def main():
                 for _ in range(args.steps)]
     for a, b in quant_ev:
         a.record(stream)
-        m.quantize(q, k, v)
+        m.prepare(q, k, v)
         b.record(stream)
     torch.cuda.synchronize()
     quant_ms = float(np.mean([a.elapsed_time(b) for a, b in quant_ev]))
     # the same with Q, K and V read from HBM: COLD_SETS copies of them in rotation
     cold_sets = [(q.clone(), k.clone(), v.clone()) for _ in range(COLD_SETS)]
-    quant_cold_ms = cold_launch_us([lambda t=t: m.quantize(*t) for t in cold_sets], stream) * 1e-3
+    quant_cold_ms = cold_launch_us([lambda t=t: m.prepare(*t) for t in cold_sets], stream) * 1e-3
     del cold_sets
     kernels = quantizer_rates(c, q, k, v, m, stream)
 
@@ -822,12 +823,13 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     # algorithmic bytes of the quantize step per element of each tensor: FP8 mode, bf16 in + FP8
-    # out (V transposed); FP4 mode, Q and K bf16 in + codes and scales (+ FP8 unless BMM1 takes
-    # the FP4 form), V bf16 in + codes, scales and bf16 dequant, then the transposed FP8 pass
+    # out (V transposed), for K and V (Q too when it is not quantized in the attention kernel);
+    # FP4 mode, Q and K bf16 in + codes and scales (+ FP8 unless BMM1 takes the FP4 form), V bf16
+    # in + codes, scales and bf16 dequant, then the transposed FP8 pass
     n = c.B * c.H * c.N * c.d
     fp4_out = 0.5 + 1.0 / 32
     if c.mode == "fp8":
-        quant_bytes = 3 * n * 3
+        quant_bytes = (2 if m.fuse_q else 3) * n * 3
     else:
         qk = 2 + fp4_out + (0 if args.native_fp4 else 1)
         quant_bytes = n * (2 * qk + (2 + fp4_out + 2) + 3)
@@ -850,6 +852,8 @@ def main():
                             "e4m3 values on the bf16 mfma"), "p_reading": args.p_reading,
                    "step": ("FP4 quantize Q,K,V (V then FP8) + attention with MXFP4 BMM1"
                             if args.native_fp4 else
+                            "quantize K,V to FP8 + fused attention quantizing bf16 Q to FP8 "
+                            "in-kernel (static scales)" if m.fuse_q else
                             "quantize Q,K,V to FP8 + fused attention (static scales)")},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",

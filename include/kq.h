@@ -164,6 +164,21 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
                                float* row_stats_or_null, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* kq_attn_quant_fwd_ws with Q given in bf16 and quantized inside the attention kernel (blog
+ * bullets 1-4, Fig. 4: the per-tensor FP8 FakeQuantize of Q feeding the first matmul).  Each
+ * element's code is E4M3(clamp(fl32(x * inv_scale_q), -448, 448)), nearest even: the codes
+ * kq_quantize_fp8_tensor writes with the same inv_scale_q, so O and the row statistics equal,
+ * bit for bit, those of quantizing Q with it and calling kq_attn_quant_fwd_ws.  Every Q element
+ * is read once, so this saves the quantizer's pass over Q and its FP8 copy.
+ * q_bf16: device bf16 [B*H][N][128], 16-byte aligned.  inv_scale_q: finite, > 0 (the
+ * quantizer's scale, kq_fp8_scales_from_amax); s_q still enters c1 as in kq_attn_quant_fwd.
+ * Every other argument, rule and error as kq_attn_quant_fwd_ws. */
+kq_status kq_attn_quant_fwd_qbf16(const void* q_bf16, float inv_scale_q, const uint8_t* k8,
+                                  const uint8_t* v8, int v_layout, int B, int H, int N, int d,
+                                  float s_q, float s_k, float s_v, float sm_scale, float* o_f32,
+                                  float* row_stats_or_null, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* SVD-Quant in FP4 for a projection GEMM (blog section "Workflow and Quantization", which names
  * SVD-Quant in FP4 beside PTQ in FP8 and FP4; the page gives none of its steps, so this is the
  * method's plainest form).  Offline, the bf16 weights W [N][K] are split into rank-r bf16

@@ -21,7 +21,7 @@ __all__ = ["KQError", "LIB_PATH", "load", "KQ_LAYOUT_ROWS", "KQ_LAYOUT_TRANSPOSE
            "kq_status_string", "kq_vt_ld", "kq_fp8_scales_from_amax", "kq_rope3_table",
            "kq_amax_calibrate", "kq_quantize_fp8_tensor", "kq_quantize_fp4_block",
            "kq_attn_quant_fwd", "kq_attn_workspace_size", "kq_attn_quant_fwd_ws",
-           "kq_attn_quant_fwd_noalloc",
+           "kq_attn_quant_fwd_noalloc", "kq_attn_quant_fwd_qbf16",
            "kq_attn_mxfp4_fwd", "kq_attn_r1_stats", "kq_attn_r1_amax", "kq_attn_r1_fwd",
            "kq_gemm_fp8", "kq_gemm_mxfp4", "kq_gemm_fp8_bf16", "kq_gemm_mxfp4_bf16",
            "kq_svdquant_down", "kq_gemm_mxfp4_svdquant", "kq_gemm_mxfp4_svdquant_bf16",
@@ -62,6 +62,8 @@ _SIGNATURES = {
                               ctypes.c_size_t, _P], _I),
     "kq_attn_quant_fwd_noalloc": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P],
                                   _I),
+    "kq_attn_quant_fwd_qbf16": ([_P, _F, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P,
+                                 ctypes.c_size_t, _P], _I),
     "kq_attn_mxfp4_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P,
                            ctypes.c_size_t, _P], _I),
     "kq_attn_r1_stats": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P,
@@ -262,6 +264,29 @@ def kq_attn_quant_fwd_ws(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_sca
         v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v), float(sm_scale),
         _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"), ws, nbytes,
         _stream(stream)), "kq_attn_quant_fwd_ws")
+
+
+def kq_attn_quant_fwd_qbf16(q, inv_scale_q: float, k8, v8t, s_q: float, s_k: float, s_v: float,
+                            sm_scale: float, o, workspace, row_stats=None,
+                            v_layout: int = KQ_LAYOUT_TRANSPOSED, stream=None):
+    """kq_attn_quant_fwd_ws with Q in bf16 [B, H, N, 128], quantized inside the kernel with
+    inv_scale_q (the codes kq_quantize_fp8_tensor forms; the result equals quantizing Q first,
+    bit for bit)."""
+    import torch
+    B, H, N, d = q.shape
+    if tuple(k8.shape) != (B, H, N, d) or tuple(o.shape) != (B, H, N, d):
+        raise KQError("k8 and o must match q's shape")
+    if v_layout == KQ_LAYOUT_TRANSPOSED and v8t.numel() != B * H * d * kq_vt_ld(N):
+        raise KQError("v8t must be [B*H, d, kq_vt_ld(N)]")
+    if row_stats is not None and row_stats.numel() != B * H * N * 2:
+        raise KQError("row_stats must be [B, H, N, 2]")
+    ws = _opt(workspace, torch.uint8, "workspace")
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(load().kq_attn_quant_fwd_qbf16(
+        _dev(q, torch.bfloat16, "q"), float(inv_scale_q), _dev(k8, torch.uint8, "k8"),
+        _dev(v8t, torch.uint8, "v8"), v_layout, B, H, N, d, float(s_q), float(s_k), float(s_v),
+        float(sm_scale), _dev(o, torch.float32, "o"), _opt(row_stats, torch.float32, "row_stats"),
+        ws, nbytes, _stream(stream)), "kq_attn_quant_fwd_qbf16")
 
 
 def kq_attn_quant_fwd_noalloc(q8, k8, v8t, s_q: float, s_k: float, s_v: float, sm_scale: float,

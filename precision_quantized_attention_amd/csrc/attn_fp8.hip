@@ -17,6 +17,10 @@
 // (E2M1 + E8M0 on the scaled MFMA) instead of their FP8 re-quantization; kMode 1, the first
 // pass of the literal FakeQuantize of the normalized P (statistics only); kMode 2, its second
 // pass (the row's M and l known, every block at the same offset).
+// With a bf16 Q (AttnParams::q_bf16, FP8 BMM1), Q's per-tensor FP8 quantization runs here
+// instead of in the FP8 tensor quantizer, with its conversion: each Q element is read by one
+// lane of one workgroup, so this saves the quantizer's read of Q and the write and re-read of
+// its codes, and the codes (hence O) are the quantizer's bit for bit.
 //
 // Matrix cores.  The page executes QK^T on FP8 (E4M3) inputs (its higher-precision
 // accumulation refers to the projection GEMM that produces Q, K, V); the reading taken here
@@ -131,6 +135,20 @@ __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 __device__ __forceinline__ uint2 bload8_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
   return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint4 bload16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Four float32 -> four E4M3 codes (byte i = value i) after the per-tensor scale: the
+// conversion of the FP8 tensor quantizer (product rounded to float32, clamped to +-448 by one
+// v_med3, then v_cvt_pk_fp8_f32, nearest even), so Q quantized here has the quantizer's codes.
+__device__ __forceinline__ uint32_t e4m3x4_q(float a, float b, float c, float d, float inv) {
+  auto sat = [](float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a * inv), sat(b * inv), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c * inv), sat(d * inv), w, true);
+  return (uint32_t)w;
 }
 
 // 4 E4M3 codes (one dword) -> 4 bf16 values (two dwords), exact.
@@ -590,6 +608,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnParams a, int
     const uint32_t sd = __builtin_amdgcn_raw_buffer_load_b32(qsr, (uint32_t)q * 4, 0, 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) qop.s[h] = (int)(sd >> (8 * (2 * h + g))) & 0xFF;
+  } else if (a.q_bf16 != nullptr) {
+    // Q given in bf16: its FP8 codes are formed here, as the FP8 tensor quantizer forms them
+    // (each Q element is read by exactly one lane of one workgroup), then widened like the codes
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q_bf16 + (int64_t)bh * N * kD, (uint32_t)N * kD * 2);
+    const uint32_t qo = ((uint32_t)q * kD + 8 * g) * 2;
+    const float inv = a.q_inv;
+    auto lo16 = [](uint32_t w) { return __uint_as_float(w << 16); };
+    auto hi16 = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint4 x = bload16_stream(qr, qo + 32 * m);
+      const uint32_t c0 = e4m3x4_q(lo16(x.x), hi16(x.x), lo16(x.y), hi16(x.y), inv);
+      const uint32_t c1 = e4m3x4_q(lo16(x.z), hi16(x.z), lo16(x.w), hi16(x.w), inv);
+      const uint2 lo = e4m3x4_to_bf16(c0), hi = e4m3x4_to_bf16(c1);
+      qop.v[m] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
   } else {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + (int64_t)bh * N * kD, (uint32_t)N * kD);
     const uint32_t qo = (uint32_t)q * kD + 8 * g;

@@ -76,6 +76,8 @@ kq_status attn_params(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, i
   const double c1 = (double)s_q * (double)s_k * (double)sm_scale * 1.4426950408889634;
   if (!isfinite(c1) || !isfinite((float)c1) || (float)c1 <= 0.0f) return KQ_ERR_INVALID_ARG;
   p->q = q8;
+  p->q_bf16 = nullptr;
+  p->q_inv = 0.0f;
   p->k = k8;
   p->q_scales = p->k_scales = nullptr;
   p->vt = v8;
@@ -304,6 +306,26 @@ kq_status kq_attn_quant_fwd_ws(const uint8_t* q8, const uint8_t* k8, const uint8
   const kq_status st = attn_params(q8, k8, v8, v_layout, B, H, N, d, s_q, s_k, s_v, sm_scale,
                                    o_f32, row_stats_or_null, &p);
   if (st != KQ_OK) return st;
+  const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
+  if (sw != KQ_OK) return sw;
+  return from_hip(kq::launch_attn_fp8(p, stream));
+}
+
+kq_status kq_attn_quant_fwd_qbf16(const void* q_bf16, float inv_scale_q, const uint8_t* k8,
+                                  const uint8_t* v8, int v_layout, int B, int H, int N, int d,
+                                  float s_q, float s_k, float s_v, float sm_scale, float* o_f32,
+                                  float* row_stats_or_null, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (!finite_pos(inv_scale_q)) return KQ_ERR_INVALID_ARG;
+  kq::AttnParams p;
+  // q_bf16 takes q8's checks (non-null, 16-byte aligned); the kernel reads it instead
+  const kq_status st = attn_params(static_cast<const uint8_t*>(q_bf16), k8, v8, v_layout, B, H, N,
+                                   d, s_q, s_k, s_v, sm_scale, o_f32, row_stats_or_null, &p);
+  if (st != KQ_OK) return st;
+  // per-(b, h) Q bytes N * 256 are addressed with 32-bit offsets (N < 2^24 holds above)
+  p.q = nullptr;
+  p.q_bf16 = static_cast<const uint16_t*>(q_bf16);
+  p.q_inv = inv_scale_q;
   const kq_status sw = attn_workspace(B, H, N, workspace, workspace_bytes, &p);
   if (sw != KQ_OK) return sw;
   return from_hip(kq::launch_attn_fp8(p, stream));

@@ -22,6 +22,8 @@ hipError_t launch_fp4_block(const uint16_t* x, int64_t rows, int d, uint8_t* cod
 
 struct AttnParams {
   const uint8_t* q;       // [BH][N][128] E4M3, or [BH][N][64] packed E2M1 (q_scales set)
+  const uint16_t* q_bf16; // FP8 BMM1 only: [BH][N][128] bf16 Q quantized in the kernel (q unused), or nullptr
+  float q_inv;            // with q_bf16: the per-tensor 1 / s_q the codes are formed with
   const uint8_t* k;       // [BH][N][128] E4M3, or [BH][N][64] packed E2M1
   const uint8_t* q_scales;  // MXFP4 BMM1: [BH][N][4] E8M0; nullptr: FP8 BMM1
   const uint8_t* k_scales;  // MXFP4 BMM1: [BH][N][4] E8M0

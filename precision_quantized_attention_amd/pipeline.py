@@ -9,6 +9,8 @@ Low-Precision Quantization", section "Workflow and Quantization" and Fig. 4):
     Q, K: [RoPE] -> [FP4 block quant] -> per-tensor FP8          (one fused kernel each)
     V:    [FP4 block quant] -> per-tensor FP8, transposed layout
     fused attention: FP8 BMM1, FP32 softmax, FP8 P, FP8 BMM2
+  (FP8 mode, one-pass P: Q's per-tensor FP8 step runs inside the attention kernel, on its one
+  read of Q, with the quantizer's codes.)
 
 Every step runs in libkq's kernels; this module only allocates outputs and passes
 pointers.  Calibration copies one float per tensor to the host to derive the static scales.
@@ -22,7 +24,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (KQ_LAYOUT_TRANSPOSED, KQError, kq_amax_calibrate, kq_attn_mxfp4_fwd, kq_attn_quant_fwd_ws,
+from . import (KQ_LAYOUT_TRANSPOSED, KQError, kq_amax_calibrate, kq_attn_mxfp4_fwd,
+               kq_attn_quant_fwd_qbf16, kq_attn_quant_fwd_ws,
                kq_attn_r1_amax, kq_attn_r1_fwd, kq_attn_r1_stats,
                kq_attn_workspace_size,
                kq_fp8_scales_from_amax, kq_quantize_fp4_block, kq_quantize_fp8_tensor,
@@ -51,10 +54,14 @@ class QuantizedSDPA:
     p_reading "r3" (default): the one-pass reading (static 1/448 scale on exp2(t - M), row sum
     after BMM2).  "r1": the literal FakeQuantize of the normalized P with a calibrated
     per-tensor amax_P, two passes (FP8 BMM1 only).
+    fuse_q (FP8 mode, "r3" only; default on there): forward() quantizes Q inside the attention
+    kernel (kq_attn_quant_fwd_qbf16, bit-identical codes and output) and leaves buf.q8
+    unwritten; quantize() still writes all three FP8 tensors.
     """
 
     def __init__(self, B, H, N, d=128, mode="fp8", positions=None, device="cuda",
-                 sm_scale=None, want_stats=False, native_fp4=False, p_reading="r3"):
+                 sm_scale=None, want_stats=False, native_fp4=False, p_reading="r3",
+                 fuse_q=None):
         if mode not in ("fp8", "fp4"):
             raise ValueError(mode)
         if native_fp4 and mode != "fp4":
@@ -64,6 +71,11 @@ class QuantizedSDPA:
             raise ValueError(p_reading)
         self.p_reading = p_reading
         self.amax_p = None
+        can_fuse = mode == "fp8" and p_reading == "r3"
+        if fuse_q and not can_fuse:
+            raise ValueError("fuse_q needs mode 'fp8' and p_reading 'r3'")
+        self.fuse_q = can_fuse if fuse_q is None else bool(fuse_q)
+        self._q_bf16 = None           # Q of the prepared forward when fuse_q
         if positions is not None and mode != "fp4":
             raise ValueError("the rotary embedding is fused into the FP4 quantizer")
         self.B, self.H, self.N, self.d, self.mode = B, H, N, d, mode
@@ -133,8 +145,21 @@ class QuantizedSDPA:
                                     device=self.device)
         return self._st4
 
+    def prepare(self, q, k, v):
+        """The per-forward quantization that precedes attention(): with fuse_q, K and V only
+        (Q is quantized inside the attention kernel); otherwise quantize()."""
+        if not self.fuse_q:
+            self.quantize(q, k, v)
+            return
+        b = self.buf
+        kq_quantize_fp8_tensor(k, self.scales["k"][1], b.k8)
+        kq_quantize_fp8_tensor(v, self.scales["v"][1], b.v8t, layout=KQ_LAYOUT_TRANSPOSED)
+        self._q_bf16 = q
+
     def quantize(self, q, k, v):
-        """Per-forward quantization of Q, K, V into the FP8 attention inputs."""
+        """Per-forward quantization of Q, K, V into the FP8 attention inputs (all three, into
+        buf; attention() then reads Q's codes from buf.q8)."""
+        self._q_bf16 = None
         b = self.buf
         if self.mode == "fp8":
             kq_quantize_fp8_tensor(q, self.scales["q"][1], b.q8)
@@ -174,13 +199,17 @@ class QuantizedSDPA:
             (qc, qs), (kc, ks) = b.fp4["q"], b.fp4["k"]
             kq_attn_mxfp4_fwd(qc, qs, kc, ks, b.v8t, self.scales["v"][0], self.sm_scale, b.o,
                               ws, row_stats=b.stats)
+        elif self._q_bf16 is not None:
+            kq_attn_quant_fwd_qbf16(self._q_bf16, self.scales["q"][1], b.k8, b.v8t,
+                                    self.scales["q"][0], self.scales["k"][0], self.scales["v"][0],
+                                    self.sm_scale, b.o, ws, row_stats=b.stats)
         else:
             kq_attn_quant_fwd_ws(b.q8, b.k8, b.v8t, self.scales["q"][0], self.scales["k"][0],
                                  self.scales["v"][0], self.sm_scale, b.o, ws, row_stats=b.stats)
         return b.o
 
     def forward(self, q, k, v):
-        self.quantize(q, k, v)
+        self.prepare(q, k, v)
         return self.attention()
 
 

@@ -82,6 +82,19 @@ def test_validation_rejects_before_any_hip_call():
              None) == UNSUPPORTED
     assert W(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, odd, 1 << 20,
              None) == INVALID
+    Fq = lib.kq_attn_quant_fwd_qbf16             # Q's scale, the attention checks, the workspace
+    assert Fq(fake, 0.0, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, None, 0,
+              None) == INVALID
+    assert Fq(fake, float("inf"), fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None,
+              None, 0, None) == INVALID
+    assert Fq(None, 2.0, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, None, 0,
+              None) == INVALID
+    assert Fq(odd, 2.0, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, None, 0,
+              None) == INVALID
+    assert Fq(fake, 2.0, fake, fake, 1, 1, 1, 128, 64, 1.0, 1.0, 1.0, 0.1, fake, None, None, 0,
+              None) == UNSUPPORTED
+    assert Fq(fake, 2.0, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, fake, None, odd,
+              1 << 20, None) == INVALID
     Z = lib.kq_attn_quant_fwd_noalloc            # the attention checks, before any HIP call
     assert Z(fake, fake, fake, 1, 1, 1, 128, 128, 1.0, 1.0, 1.0, 0.1, None, None, None) == INVALID
     assert Z(fake, fake, fake, 1, 1, 1, 128, 64, 1.0, 1.0, 1.0, 0.1, fake, None, None) == UNSUPPORTED

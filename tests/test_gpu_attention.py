@@ -29,6 +29,8 @@ def _run(bits, mode="fp8", positions=None, stats=False):
     m.calibrate(*x)
     o = m.forward(*x)
     torch.cuda.synchronize()
+    if m.fuse_q:
+        m.quantize(*x)          # forward() formed Q's codes in the kernel: write them for the checks
     return m, o
 
 
@@ -244,6 +246,7 @@ def test_attention_beyond_2_31_elements():
     m = QuantizedSDPA(B, H, N, d)
     m.calibrate(*x)
     o = m.forward(*x)
+    m.quantize(*x)              # Q's codes into buf.q8 for the checks below (o is unchanged)
     torch.cuda.synchronize()
     del x
     qz = OP.quantize_inputs(*base)
@@ -321,6 +324,7 @@ def test_attention_scale_ranges(qk, vs, sm):
     m = QuantizedSDPA(1, 2, 300, 128, sm_scale=sm, want_stats=True)
     m.calibrate(*x)
     o = m.forward(*x)
+    m.quantize(*x)
     torch.cuda.synchronize()
     qz = OP.quantize_inputs(*bits)
     _check_codes(m, qz)
@@ -400,3 +404,64 @@ def test_attention_every_e4m3_code_in_q_and_k():
     O, _, _ = A.attention_r3(q8, k8, v8, s_q, s_k, s_v, sm)
     _compare(o.cpu().numpy(), O, "every E4M3 code")
     assert F.e4m3_decode(codes).max() == 448.0
+
+
+def _fused_vs_unfused(m, x):
+    """O and row statistics of forward() (Q quantized in the attention kernel) and of
+    quantize() + attention() (Q through the FP8 quantizer), each with the pipeline's workspace,
+    and the single pass of both without one."""
+    o_f = m.forward(*x).clone()
+    st_f = m.buf.stats.clone()
+    m.quantize(*x)
+    o_u = m.attention().clone()
+    st_u = m.buf.stats.clone()
+    b = m.buf
+    sc = [m.scales[n][0] for n in "qkv"]
+    o1_f, o1_u = torch.empty_like(b.o), torch.empty_like(b.o)
+    kq.kq_attn_quant_fwd_qbf16(x[0], m.scales["q"][1], b.k8, b.v8t, *sc, m.sm_scale, o1_f, None)
+    kq.kq_attn_quant_fwd(b.q8, b.k8, b.v8t, *sc, m.sm_scale, o1_u)
+    torch.cuda.synchronize()
+    assert torch.equal(o_f, o_u) and torch.equal(st_f, st_u)
+    assert torch.equal(o1_f, o1_u)
+    return o_f
+
+
+@pytest.mark.parametrize("case", ["cfg1", "ragged300", "q_past_calibration", "cfg3"])
+def test_fused_q_quantization_equals_the_quantizer(case):
+    """FP8 mode's forward() quantizes Q inside the attention kernel (kq_attn_quant_fwd_qbf16)
+    with the FP8 quantizer's conversion, so O and the row statistics equal, bit for bit, those of
+    quantizing Q first: single pass and key split (cfg3's last round), ragged N, and Q scaled
+    past its calibrated amax so that both sides clamp codes at +-448."""
+    print(f"fused Q quantization: {case}", flush=True)
+    bits = (W.qkv_bits(1) if case == "cfg1" else W.qkv_bits(3) if case == "cfg3"
+            else _scaled_bits(1.0, 1.0, 2300 if case == "ragged300" else 2400))
+    x = [to_dev(b) for b in bits]
+    B, H, N, d = x[0].shape
+    m = QuantizedSDPA(B, H, N, d, want_stats=True)
+    assert m.fuse_q
+    m.calibrate(*x)
+    if case == "q_past_calibration":
+        x[0] = x[0] * 4                          # exact in bf16; |q| * inv reaches 4 * 448
+    _fused_vs_unfused(m, x)
+    if case == "q_past_calibration":
+        q8 = m.buf.q8.cpu().numpy()
+        assert np.any((q8 & 0x7F) == 0x7E), "no code clamped at 448"
+
+
+def test_fused_q_every_bf16_value():
+    """Q holding every finite bf16 value (65280 of them, both signs, subnormals, values far past
+    the clamp) in a 512 x 128 tile: the in-kernel codes equal the quantizer's, so the fused and
+    the unfused attention agree bit for bit."""
+    bits = np.arange(65536, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]                      # drop Inf and NaN
+    rng = np.random.default_rng(11)
+    qb = np.concatenate([bits, rng.choice(bits, 512 * 128 - bits.size)])
+    rng.shuffle(qb)
+    qb = qb.reshape(1, 1, 512, 128)
+    kb = W.random_bits(1, 1, 512, 128, seed=2500, outliers=True)
+    vb = W.random_bits(1, 1, 512, 128, seed=2501, outliers=True)
+    x = [to_dev(b) for b in (qb, kb, vb)]
+    m = QuantizedSDPA(1, 1, 512, 128, want_stats=True)
+    m.calibrate(x[1], x[1], x[2])                # Q's scale from K's amax: most of Q clamps
+    _fused_vs_unfused(m, x)
+
