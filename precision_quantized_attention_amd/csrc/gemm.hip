@@ -14,10 +14,9 @@
 // MFMA (the scaled form for MXFP4, the unscaled one for FP8; 128 accumulator registers).  The
 // product is computed transposed, D = B_sub · A_sub^T, so each lane owns one row m of C.  A
 // k-step moves 64 bytes of each operand row (64 FP8 or 128 FP4 elements) through LDS: 64-byte
-// rows with the 16-byte chunks swizzled (conflict-free staging writes and operand reads), three
-// stages, a step's tile
-// written two steps before it is multiplied; the HBM loads of a step are issued two steps
-// before their LDS store (two register sets); MXFP4 scales go through a two-slot LDS ring,
+// rows with the 16-byte chunks swizzled (conflict-free operand reads), three stages, each
+// step's tile loaded from HBM straight into its stage (buffer_load ... lds) two steps before it
+// is multiplied; MXFP4 scales go through a two-slot LDS ring,
 // fetched 16 bytes (four k-steps) per row at a time and read once per two steps, the MFMA's
 // scale select picking each step's byte.  Ping-pong: the two waves of a SIMD run half a
 // step apart, one issuing its step's eight (FP8) or sixteen (FP4) MFMAs while the other
@@ -49,9 +48,10 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kTile = 256;            // workgroup tile of C (M and N)
 constexpr int kThreads = 512;         // 8 waves, two per SIMD
 constexpr int kRowBytes = 64;         // bytes of one operand row per k-step
-// LDS stage rows: chunk c (16 bytes) of row R at 16 * (c ^ ((R >> 2) & 3)).  A staging store
-// instruction covers rows 4q .. 4q+3 x chunks 0-3 in each 16-lane group and an operand read 16
-// consecutive rows x one chunk; with the swizzle both touch 16 distinct 16-byte bank groups.
+// LDS stage rows: chunk c (16 bytes) of row R at 16 * (c ^ ((R >> 2) & 3)).  An operand read
+// covers 16 consecutive rows x one chunk per 16-lane group; with the swizzle it touches 16
+// distinct 16-byte bank groups.  A wave's share of a stage (16 rows, 1 KB) is contiguous, the
+// block a 16-byte LDS-direct load fills (lane l at 16 l).
 constexpr int kPitch = kRowBytes;
 constexpr int kOpStage = kTile * kPitch;            // 16384 bytes per operand
 constexpr int kStage = 2 * kOpStage;                // A, B codes
@@ -80,6 +80,12 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// 16 bytes per lane from buffer r at off into LDS at lds_wave + 16 * lane (lds_wave uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave, 16, off,
+                                           0, 0, 0);
 }
 
 // A wave holds 8 tiles of 32 x 32 (128 accumulator registers) and two waves share each SIMD.
@@ -214,16 +220,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.a, (uint32_t)p.m * row_bytes);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(p.b, (uint32_t)p.n * row_bytes);
 
-  // staging: each operand tile is 256 rows x 4 chunks of 16 bytes; thread t owns chunks t and
-  // t + 512 of both (rows t/4 and t/4 + 128, chunk t % 4).  FP4 scales: thread t owns the E8M0
+  // staging: each operand tile is 256 rows x 4 chunks of 16 bytes, loaded straight into LDS;
+  // thread t fills LDS slots t and t + 512 of both (rows t/4 and t/4 + 128, slot t % 4), i.e.
+  // it loads the chunk the swizzle puts there, so 4 consecutive lanes still read one row's 64
+  // contiguous bytes, and wave w fills the 1 KB blocks of rows 16w .. 16w + 15 (and + 128).
+  // FP4 scales: thread t owns the E8M0
   // bytes of operand row t (A rows 0-255, then B rows), fetched 16 bytes (4 k-steps) at a
   // time four steps ahead and written to the ring slot of their block; one dword per row per
   // step would touch a 128-byte line for 4 useful bytes, every step.
-  const int crow = tid >> 2, cchunk = tid & 3;
-  const uint32_t goff_a = (uint32_t)(mt * kTile + crow) * row_bytes + 16 * cchunk;
-  const uint32_t goff_b = (uint32_t)(nt * kTile + crow) * row_bytes + 16 * cchunk;
+  const int crow = tid >> 2, gchunk = (tid & 3) ^ ((crow >> 2) & 3);
+  const uint32_t goff_a = (uint32_t)(mt * kTile + crow) * row_bytes + 16 * gchunk;
+  const uint32_t goff_b = (uint32_t)(nt * kTile + crow) * row_bytes + 16 * gchunk;
   const uint32_t row128 = 128u * row_bytes;
-  const int loff = crow * kPitch + 16 * (cchunk ^ ((crow >> 2) & 3));   // rows crow and crow + 128
+  const int wlds = __builtin_amdgcn_readfirstlane(w) * 16 * kPitch;    // the wave's 1 KB of a stage
   const bool sc_a = __builtin_amdgcn_readfirstlane(tid) < 256;
   const __amdgpu_buffer_rsrc_t scr =
       make_rsrc(sc_a ? p.a_scales : p.b_scales, (uint32_t)(sc_a ? p.m : p.n) * sc_bytes);
@@ -237,23 +246,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     return make_uint4(bload4(scr, o_), bload4(scr, o_ + 4), bload4(scr, o_ + 8), bload4(scr, o_ + 12));
   };
 
-  uint4 xa0[2], xa1[2], xb0[2], xb1[2];
-#define KQ_LOAD(s, R)                                                     \
-  {                                                                       \
-    const uint32_t o_ = (uint32_t)(s) * kRowBytes;                        \
-    xa0[R] = bload16(ar, goff_a + o_);                                    \
-    xa1[R] = bload16(ar, goff_a + row128 + o_);                           \
-    xb0[R] = bload16(br, goff_b + o_);                                    \
-    xb1[R] = bload16(br, goff_b + row128 + o_);                           \
+  // step s's tile of both operands into LDS stage `stage`
+#define KQ_DMA(s, stage)                                                          \
+  {                                                                               \
+    uint8_t* st_ = lds + (stage) * kStage + wlds;                                 \
+    const uint32_t o_ = (uint32_t)(s) * kRowBytes;                                \
+    dma16(ar, st_, goff_a + o_);                                                  \
+    dma16(ar, st_ + 128 * kPitch, goff_a + row128 + o_);                          \
+    dma16(br, st_ + kOpStage, goff_b + o_);                                       \
+    dma16(br, st_ + kOpStage + 128 * kPitch, goff_b + row128 + o_);               \
   }
-#define KQ_STORE(stage, R)                                                \
-  {                                                                       \
-    uint8_t* st_ = lds + (stage) * kStage;                                \
-    *reinterpret_cast<uint4*>(st_ + loff) = xa0[R];                       \
-    *reinterpret_cast<uint4*>(st_ + loff + 128 * kPitch) = xa1[R];        \
-    *reinterpret_cast<uint4*>(st_ + kOpStage + loff) = xb0[R];            \
-    *reinterpret_cast<uint4*>(st_ + kOpStage + loff + 128 * kPitch) = xb1[R]; \
-  }
+  // a loop barrier without a memory fence: the LDS operations drained, not the loads into LDS
+  // (a fence would wait for those too; their visibility comes from each wave's vmcnt(0) at the
+  // start of its next memory half, before the next barrier)
+#define KQ_BAR() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
   // operand reads of lane (r, g): chunks g and g + 2 of its rows (sub-tile rows are 32 apart,
   // so every row of the lane has the swizzle of r)
@@ -294,23 +300,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     }
   }
 
-  // Step s stores register set s % 2 (step s + 2, fetched in step s - 2) into stage (s + 2) % 3
-  // (read last in step s - 1), fetches step s + 4 into the same set and multiplies stage s % 3
-  // (stored in step s - 2).  Past the last step the fetches read bytes of the next rows (or
-  // zeros past the end) into stages nothing reads.
+  // Step s waits for this wave's loads into LDS (steps s and s + 1, issued in steps s - 2 and
+  // s - 1), reads its operands from stage s % 3, then loads step s + 2 into stage (s + 2) % 3
+  // (read last in step s - 1) and multiplies.  The load is issued after the operand reads: the
+  // compiler cannot tell the stages apart and waits for every outstanding load into LDS before
+  // a read from LDS, so a load issued before the reads would be waited for at once.  Past the
+  // last step the loads read bytes of the next rows (or zeros past the end) into stages
+  // nothing reads.
   uint4 xq = make_uint4(0, 0, 0, 0);     // FP4: scale block of the next ring write
   if constexpr (kFP4) {
     ring_put(ring + wbase, ring_order(sload(0)));
     xq = sload(1);
   }
-  KQ_LOAD(0, 0);
-  KQ_STORE(0, 0);
-  KQ_LOAD(1, 1);
-  KQ_STORE(1, 1);
-  KQ_LOAD(2, 0);
-  KQ_FENCE();
-  KQ_LOAD(3, 1);
-  KQ_FENCE();
+  KQ_DMA(0, 0);
+  KQ_DMA(1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
   __syncthreads();
   // Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 run half a step apart.  Each step of a
   // wave is a memory part (staging, fetch, operand reads) and a matrix part (the MFMAs), each
@@ -320,26 +324,24 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   if (grp == 1) __syncthreads();
   KOps<kFP4> ops;
   int st_mul = 0, st_wr = 2;
-  // KQ_STEP(s, R, RING): R = s mod 2 (the fetch register set, and the step's parity within its
-  // scale pair), RING = (s mod 4 == 0)
+  // KQ_STEP(s, R, RING): R = s mod 2 (the step's parity within its scale pair),
+  // RING = (s mod 4 == 0)
 #define KQ_STEP(s_, R_, RING_)                                                     \
   {                                                                               \
-    if (kFP4 && (RING_)) {                                                        \
-      /* scale block (s_)/4 + 1 into its slot (read last in step (s_) - 2), then   \
-         fetch block (s_)/4 + 2 */                                                \
+    /* scale block (s_)/4 + 1 into its ring slot (read last in step (s_) - 2) */   \
+    if (kFP4 && (RING_))                                                          \
       ring_put(ring + ((((s_) >> 2) + 1) & 1) * kRingSlot + wbase, ring_order(xq)); \
-      xq = sload(((s_) >> 2) + 2);                                                \
-    }                                                                             \
-    KQ_STORE(st_wr, R_);                                                          \
-    KQ_LOAD((s_) + 4, R_);                                                        \
+    __builtin_amdgcn_s_waitcnt(0x0F70);        /* vmcnt(0) */                     \
     kread<kFP4, (R_) == 0>(ops, lds + st_mul * kStage,                            \
                 ring + (((s_) >> 2) & 1) * kRingSlot + 2048 * (((s_) >> 1) & 1),  \
                 rbase_n, rbase_m, rbase_n2, rbase_m2, sbase_n, sbase_m);          \
-    __syncthreads();                                                              \
+    KQ_DMA((s_) + 2, st_wr);                                                      \
+    if (kFP4 && (RING_)) xq = sload(((s_) >> 2) + 2);   /* scale block s/4 + 2 */ \
+    KQ_BAR();                                                                     \
     __builtin_amdgcn_s_setprio(1);                                                \
     kmma<kFP4, (R_)>(acc, ops);                                                   \
     __builtin_amdgcn_s_setprio(0);                                                \
-    __syncthreads();                                                              \
+    KQ_BAR();                                                                     \
     st_mul = st_mul == 2 ? 0 : st_mul + 1;                                        \
     st_wr = st_wr == 2 ? 0 : st_wr + 1;                                           \
   }
@@ -356,9 +358,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   if (s + 2 < nsteps) KQ_STEP(s + 2, 0, false);
 #undef KQ_STEP
   if (grp == 0) __syncthreads();
-#undef KQ_LOAD
-#undef KQ_STORE
+#undef KQ_DMA
+#undef KQ_BAR
 
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // the last steps' loads into LDS landed
   // epilogue: lane (r, g) owns row m = mt*256 + wm*64 + 32 mi + r and, for each sub-tile ni,
   // columns n = nt*256 + wn*128 + 32 ni + 8q + 4g .. +3 (q = 0..3).  The wave's 64 x 128 tile
   // leaves through the wave's own 8 KB of the (now idle) stages, 32 rows by 256 bytes at a
